@@ -1,0 +1,119 @@
+"""Speculative acceptance: greedy and rejection sampling (oracle, test infrastructure).
+
+MagicDec Section 3.1 takes the speculative-decoding procedure of Leviathan et al.: the draft
+proposes gamma tokens, the target scores gamma + 1 positions in one pass, and Eq. (1) gives
+the expected number of emitted tokens, Omega(gamma, alpha) = (1 - alpha^(gamma+1)) /
+(1 - alpha), for a per-position acceptance rate alpha. Section 5.1 (Setup) runs every
+end-to-end experiment with greedy decoding. The paper does not print the acceptance rule;
+the readings taken here:
+
+Greedy (temperature 0). Draft token x_i is accepted while it equals the target's argmax at
+position i (ties go to the lowest token id). At the first mismatch i the target's argmax at
+i is emitted instead; if all gamma drafts match, the target's argmax at position gamma is
+appended. So 1 .. gamma + 1 tokens are emitted.
+
+Rejection sampling (temperature t > 0). p_i = softmax(target_i / t), q_i = softmax(draft_i / t).
+Position i < gamma accepts x_i when u_i < p_i(x_i) / q_i(x_i), u_i a uniform in (0, 1). At the
+first rejection i the emitted token is drawn from the residual max(0, p_i - q_i) (or from p_i
+when the residual is all zero); if every draft token is accepted, an extra token is drawn
+from p_gamma. Draws use an exponential race: token y = argmin_x E_x / w(x) over w(x) > 0 with
+E_x = -log u'_x, which selects y with probability w(y) / sum w (ties: lowest id). The
+uniforms come from the Philox layout of oracle.philox.
+
+Outputs: out_tokens int32 [B, gamma + 1] (emitted tokens, then -1), num_accepted int32 [B]
+(the number of accepted draft tokens, 0 .. gamma).
+"""
+
+import numpy as np
+
+from .philox import accept_uniform, race_uniforms
+
+
+def softmax(z, temperature):
+    """softmax(z / temperature) in float64."""
+    x = np.asarray(z, dtype=np.float64) / float(temperature)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def argmax_lowest(z):
+    """Index of the maximum, the lowest index on ties."""
+    z = np.asarray(z)
+    return int(np.flatnonzero(z == z.max())[0])
+
+
+def exponential_race(weights, u):
+    """argmin_x (-log u_x) / weights_x over weights_x > 0; ties to the lowest x."""
+    weights = np.asarray(weights, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    live = weights > 0
+    keys = np.full(weights.shape, np.inf)
+    keys[live] = -np.log(u[live]) / weights[live]
+    return argmax_lowest(-keys)
+
+
+def greedy_accept(target, tokens):
+    """Greedy acceptance. target [B, gamma + 1, V]; tokens [B, gamma]."""
+    B, T, _ = target.shape
+    gamma = T - 1
+    out = np.full((B, T), -1, dtype=np.int32)
+    n_acc = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        i = 0
+        while i < gamma and argmax_lowest(target[b, i]) == int(tokens[b, i]):
+            out[b, i] = tokens[b, i]
+            i += 1
+        out[b, i] = argmax_lowest(target[b, i])
+        n_acc[b] = i
+    return out, n_acc
+
+
+def rejection_accept_one(p_rows, q_rows, tokens, u_accept, race_u):
+    """Rejection sampling for one sequence from its probability rows.
+
+    p_rows [gamma + 1, V] and q_rows [gamma, V] are target and draft probabilities;
+    u_accept(i) gives the acceptance uniform of position i and race_u(i) the race uniforms
+    [V] at emitting position i. Returns (emitted token list, number accepted).
+    """
+    gamma = q_rows.shape[0]
+    emitted = []
+    for i in range(gamma):
+        x = int(tokens[i])
+        if u_accept(i) < p_rows[i, x] / q_rows[i, x]:
+            emitted.append(x)
+            continue
+        residual = np.maximum(p_rows[i] - q_rows[i], 0.0)
+        if residual.sum() == 0.0:
+            residual = p_rows[i]
+        emitted.append(exponential_race(residual, race_u(i)))
+        return emitted, i
+    emitted.append(exponential_race(p_rows[gamma], race_u(gamma)))
+    return emitted, gamma
+
+
+def rejection_accept(target, draft, tokens, temperature, seed, offset):
+    """Rejection-sampling acceptance with Philox uniforms.
+
+    target [B, gamma + 1, V], draft [B, gamma, V] logits; tokens [B, gamma].
+    """
+    B, T, V = target.shape
+    gamma = T - 1
+    out = np.full((B, T), -1, dtype=np.int32)
+    n_acc = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        p_rows = np.stack([softmax(target[b, i], temperature) for i in range(T)])
+        q_rows = np.stack([softmax(draft[b, i], temperature) for i in range(gamma)])
+        emitted, n = rejection_accept_one(
+            p_rows, q_rows, tokens[b],
+            lambda i, b=b: accept_uniform(seed, offset, b, i),
+            lambda i, b=b: race_uniforms(seed, offset, b, i, V))
+        out[b, : len(emitted)] = emitted
+        n_acc[b] = n
+    return out, n_acc
+
+
+def spec_accept(target, draft, tokens, temperature, seed=0, offset=0):
+    """Greedy when temperature == 0, rejection sampling otherwise."""
+    if temperature == 0:
+        return greedy_accept(target, tokens)
+    return rejection_accept(target, draft, tokens, temperature, seed, offset)
