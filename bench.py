@@ -1,0 +1,259 @@
+"""Throughput of the sparse-KV self-speculative decoding hot path on one MI355X.
+
+One step = one pass of every call of the path over one batch of the workload (default: the
+Llama-3.1-8B-shaped layer, batch 64, 32000-token context, gamma 4):
+  snapkv_select (SnapKV budget 512 from the prompt), kvss_streaming_set (sink 16 + window 496),
+  draft_attn_sparse over the StreamingLLM set, verify_attn_full (gamma + 1 causal queries),
+  draft_attn_sparse over the SnapKV set, spec_accept (rejection sampling, temperature 1).
+The verify call sits between the two drafts, so the 256 MB last-level cache cannot serve the
+second draft from the first. Inputs are resident in HBM before the timed region; the timed
+region allocates nothing.
+
+value = algorithmic bytes of the whole step / step time (GB/s). Per call it also reports the
+time (HIP events on the launching stream), GB/s, fraction of the 8 TB/s HBM peak and tokens/s.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV-attn HBM GB/s (% peak) + verify/draft tokens/s, B=64 S=32000, 1 GPU"
+
+
+def algorithmic_bytes(wl, P, T, sink, window, V):
+    """Bytes each call must move (inputs read once, outputs written once); per the definitions:
+    verify: all K and V rows of every sequence + Q + fp32 O and LSE; draft: the attended K and V
+    rows + index list + Q + O; SnapKV: the K prompt read once + Q_obs + indices; accept: every
+    logit row once."""
+    eb = 2 if wl.dtype == "bf16" else 4
+    Hq, Hkv, D, B = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, len(P)
+    budget, w, _ = wl.snapkv
+    L_verify = P + T
+    L_draft = P + 1
+    row = Hkv * D * 2 * eb                                      # one K row + one V row, all heads
+    q_out = lambda rows: rows * Hq * D * (eb + 4) + rows * Hq * 4
+    out = {}
+    out["verify"] = int(L_verify.sum()) * row + q_out(B * T)
+    stream_rows = sum(min(int(L), sink + window) for L in L_draft)
+    out["draft_streaming"] = stream_rows * row + B * Hkv * sink * 4 + q_out(B)
+    k = budget - w
+    snap_rows = sum(min(k, max(int(p) - w, 0)) + (int(L) - max(int(p) - w, 0)) for p, L in zip(P, L_draft))
+    out["draft_snapkv"] = snap_rows * row + B * Hkv * k * 4 + q_out(B)
+    out["snapkv_select"] = int(P.sum()) * Hkv * D * eb + B * Hq * w * D * eb + B * Hkv * k * 4
+    out["streaming_set"] = B * Hkv * sink * 4 + B * 12
+    out["spec_accept"] = B * (2 * (T - 1) + 1) * V * 4 + B * T * 4
+    return out
+
+
+def cpu_baseline(wl, ns, sink, window, budget_s=12.0):
+    """The oracle, as written, timed on this host on a bounded sample of the same step:
+    sequence 0 / KV head 0 for the attention and selection calls, sequence 0 for acceptance."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.accept as oacc
+    import oracle.attention as oatt
+    import oracle.snapkv as osnap
+    import oracle.streaming as ostream
+    from kv_sparse_speculative_amd.synth import to_numpy
+
+    cores = len(os.sched_getaffinity(0))
+    budget, w, pool = wl.snapkv
+    P = ns.prompt_lens_np
+    T = ns.T
+    Hkv = wl.num_kv_heads
+    eb = 2 if wl.dtype == "bf16" else 4
+    row = wl.head_dim * 2 * eb
+    # host copies of sequence 0's blocks only
+    blocks = ns.block_table_np[0][ns.block_table_np[0] >= 0]
+    import torch
+    idx = torch.as_tensor(blocks.astype(np.int64), device=ns.k_cache.device)
+    kh = to_numpy(ns.k_cache.index_select(0, idx))
+    vh = to_numpy(ns.v_cache.index_select(0, idx))
+    table = np.full((1, ns.block_table_np.shape[1]), -1, dtype=np.int32)
+    table[0, : len(blocks)] = np.arange(len(blocks))
+    q_obs = to_numpy(ns.q_obs[:1])
+    q_draft = to_numpy(ns.q_draft[:1])
+    q_ver = to_numpy(ns.q_verify[:1])
+    tl = to_numpy(ns.target_logits[:1])
+    dl = to_numpy(ns.draft_logits[:1])
+    tok = to_numpy(ns.draft_tokens[:1])
+    p0 = P[:1]
+    nbytes = 0
+    steps = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while True:
+            c = osnap.snapkv_scores(q_obs, kh, table, p0, w, 1 / math.sqrt(wl.head_dim), pairs=[(0, 0)])
+            sel = np.full((1, Hkv, budget - w), -1, dtype=np.int32)
+            n = max(int(p0[0]) - w, 0)
+            sel[0, 0] = -1
+            keep = osnap.top_k_positions(osnap.max_pool(c[0, 0, :n], pool), budget - w)
+            sel[0, 0, : len(keep)] = keep
+            cnt = np.array([len(keep)], dtype=np.int32)
+            s_idx, s_cnt, s_tail = ostream.streaming_set(p0 + 1, Hkv, sink, window)
+            scale = 1 / math.sqrt(wl.head_dim)
+            oatt.draft_attention(q_draft, kh, vh, table, p0 + 1, s_idx, s_cnt, s_tail, scale, pairs=[(0, 0)])
+            oatt.verify_attention(q_ver, kh, vh, table, p0 + T, scale, pairs=[(0, 0)])
+            oatt.draft_attention(q_draft, kh, vh, table, p0 + 1, sel, cnt, p0 - w, scale, pairs=[(0, 0)])
+            oacc.spec_accept(tl, dl, tok, 1.0, seed=1, offset=0)
+            steps += 1
+            nbytes += (int(p0[0]) + T) * row                           # verify, one KV head
+            nbytes += (min(int(p0[0]) + 1, sink + window)) * row       # streaming draft
+            nbytes += (len(keep) + w + 1) * row                        # SnapKV draft
+            nbytes += int(p0[0]) * wl.head_dim * eb                    # SnapKV K read
+            nbytes += (2 * (T - 1) + 1) * tl.shape[-1] * 4             # acceptance rows
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{steps} step(s) of sequence 0 / KV head 0 (SnapKV select, StreamingLLM "
+                       f"draft, verify, SnapKV draft) plus sequence 0's acceptance, "
+                       f"{dt:.1f} s wall")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path is not sharded across GPUs (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_sparse_speculative_amd import kvss
+    from kv_sparse_speculative_amd.synth import generate
+    from kv_sparse_speculative_amd.workloads import HEADLINE, WORKLOADS
+
+    wl = WORKLOADS[args.workload or HEADLINE]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    ns = generate(wl, device=dev)
+    B, T, D = ns.batch, ns.T, wl.head_dim
+    P = ns.prompt_lens_np
+    budget, w, pool = wl.snapkv
+    sink, window = wl.streaming or (16, 496)
+    maxP = int(P.max())
+    kv_p = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.prompt_lens, maxP)
+    kv_d = kv_p.with_lens(ns.kv_lens_draft, maxP + 1)
+    kv_v = kv_p.with_lens(ns.kv_lens_verify, maxP + T)
+    tail = (ns.prompt_lens - w).contiguous()
+
+    # outputs and workspaces allocated once, outside the timed region
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    o_ver = torch.empty((B, wl.num_q_heads, T, D), **f32)
+    l_ver = torch.empty((B, wl.num_q_heads, T), **f32)
+    o_ds = torch.empty((B, wl.num_q_heads, D), **f32)
+    o_dk = torch.empty((B, wl.num_q_heads, D), **f32)
+    ws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    snap_ws = torch.empty(kvss.lib().kvss_snapkv_workspace_bytes(
+        __import__("ctypes").byref(kv_p.desc()), wl.num_q_heads, w, budget), dtype=torch.uint8, device=dev)
+    sel = torch.empty((B, wl.num_kv_heads, budget - w), **i32)
+    cnt = torch.empty(B, **i32)
+    s_idx = torch.empty((B, wl.num_kv_heads, sink), **i32)
+    s_cnt = torch.empty(B, **i32)
+    s_tail = torch.empty(B, **i32)
+    acc_tok = torch.empty((B, T), **i32)
+    acc_n = torch.empty(B, **i32)
+    stream = torch.cuda.current_stream()
+    calls = ["snapkv_select", "streaming_set", "draft_streaming", "verify", "draft_snapkv", "spec_accept"]
+    state = {}
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        kvss.snapkv_select(kv_p, ns.q_obs, w, pool, budget, sel_idx=sel, sel_count=cnt,
+                           workspace=snap_ws)
+        mark(1)
+        kvss.kvss_streaming_set(ns.kv_lens_draft, wl.num_kv_heads, sink, window, sel_idx=s_idx,
+                                sel_count=s_cnt, tail_lo=s_tail)
+        mark(2)
+        kvss.draft_attn_sparse(kv_d, ns.q_draft, s_idx, s_cnt, s_tail, window, out=o_ds,
+                               want_lse=False, workspace=ws)
+        mark(3)
+        kvss.verify_attn_full(kv_v, ns.q_verify, out=o_ver, lse=l_ver, workspace=ws)
+        mark(4)
+        kvss.draft_attn_sparse(kv_d, ns.q_draft, sel, cnt, tail, w + 1, out=o_dk, want_lse=False,
+                               workspace=ws)
+        mark(5)
+        out = kvss.spec_accept(ns.target_logits, ns.draft_logits, ns.draft_tokens, 1.0,
+                               seed=1234, offset=state.setdefault("offset", 0), out_tokens=acc_tok,
+                               num_accepted=acc_n, workspace=ws)
+        state["offset"] += 1
+        mark(6)
+        return out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {c: 0.0 for c in calls}
+    for ev in events:
+        for i, c in enumerate(calls):
+            per_call[c] += ev[i].elapsed_time(ev[i + 1]) / args.steps
+    ms_step = wall * 1e3 / args.steps
+
+    nbytes = algorithmic_bytes(wl, P, T, sink, window, ns.vocab)
+    total_bytes = sum(nbytes.values())
+    detail = {}
+    for c in calls:
+        ms = per_call[c]
+        gbs = nbytes[c] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        d = {"ms": round(ms, 4), "GB_per_s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4),
+             "bytes": nbytes[c]}
+        if c == "verify":
+            d["tokens_per_s"] = round(B * T / (ms * 1e-3), 1)
+        if c.startswith("draft"):
+            d["tokens_per_s"] = round(B / (ms * 1e-3), 1)
+        detail[c] = d
+    v = detail["verify"]
+    result = {
+        "metric": METRIC,
+        "value": round(total_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "context": maxP, "gamma": ns.gamma,
+                   "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": D,
+                   "snapkv_budget": budget, "streaming": [sink, window], "vocab": ns.vocab},
+        "roofline": {"bound": "hbm", "achieved": v["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": v["frac_peak"], "traffic": None, "kernel": "verify_attn_full"},
+        "calls": detail,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, ns, sink, window)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * kvss.h -- C ABI of libkvss: the KV-cache hot path of sparse-KV self-speculative decoding
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "MagicDec: Breaking the Latency-Throughput Tradeoff for Long Context
+ * Generation with Speculative Decoding" (arXiv 2408.11049v5). Its cost model names the three
+ * timed steps of one speculative round -- KV selection T_select(B,S,K) and sparse draft
+ * decoding T_D(B,K) (Section 4.1, Eq. (3)), verification of gamma tokens T_V(B,S,gamma)
+ * (Section 3.1, Eq. (2)) -- and the accepted-token count Omega(gamma, alpha) (Section 3.1,
+ * Eq. (1)). Each maps to one call below:
+ *
+ *   snapkv_select      T_select : static SnapKV selection at prefill (Section 4.4, App. A.1)
+ *   kvss_streaming_set T_select : StreamingLLM sink + window set (Section 5.1, Table 1)
+ *   draft_attn_sparse  T_D      : one draft query per sequence over a sparse subset
+ *   verify_attn_full   T_V      : gamma + 1 causal queries per sequence over the full cache
+ *   spec_accept        Omega    : greedy / rejection-sampling acceptance
+ *
+ * Conventions (all calls)
+ *   - Every pointer argument that names a tensor is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains device memory. Scratch space comes from the
+ *     caller's `workspace` buffer, whose required size the matching *_workspace_bytes query
+ *     returns for the same shape arguments (0 is a valid size; workspace may then be NULL).
+ *     A workspace must not be shared by calls that may run concurrently.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls enqueue
+ *     kernels and return without synchronising; outputs are valid once the stream has
+ *     reached the enqueued work.
+ *   - Return value: KVSS_OK (0) or a negative KVSS_E* code. All argument checks run on the
+ *     host before any HIP call; on error nothing is enqueued and kvss_last_error() returns a
+ *     thread-local message. No C++ exception crosses this boundary.
+ *   - Results are bitwise deterministic for fixed inputs and shapes (no floating-point
+ *     atomics, fixed split plans).
+ *   - Tensors are dense, row-major, in the shapes given; strides are not accepted.
+ */
+#ifndef KVSS_H
+#define KVSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KVSS_API __attribute__((visibility("default")))
+#else
+#define KVSS_API
+#endif
+
+/* Status codes. */
+#define KVSS_OK 0
+#define KVSS_EINVAL (-1)        /* bad shape, pointer, length or budget                     */
+#define KVSS_EUNSUPPORTED (-2)  /* dtype, head_dim, block size or row count not compiled     */
+#define KVSS_EWORKSPACE (-3)    /* workspace smaller than the *_workspace_bytes query        */
+#define KVSS_EHIP (-4)          /* a HIP launch failed; the message carries the HIP string   */
+
+/* Storage types of K, V and queries. Attention outputs are always float32. */
+#define KVSS_F32 0
+#define KVSS_BF16 1
+
+/*
+ * Paged KV cache of one layer (MagicDec Sections 1 and 3.2: the per-layer KV cache is the
+ * dominant bandwidth term; the paper fixes no layout, this library uses paged blocks).
+ *   k, v        [num_blocks, num_kv_heads, block_size, head_dim] of `dtype`
+ *   block_table int32 [batch, max_blocks]: logical row j of sequence b is physical block
+ *               block_table[b, j / block_size], offset j % block_size. Entries past a
+ *               sequence's last block are never read.
+ *   kv_lens     int32 [batch] (device): rows cached per sequence.
+ *   max_kv_len  host-side upper bound of kv_lens, used to size launches; it must satisfy
+ *               max_kv_len <= max_blocks * block_size. Kernels clamp kv_lens[b] to it.
+ * Kernels that meet a block id outside [0, num_blocks) write NaN to the outputs of the
+ * affected sequence instead of reading out of bounds.
+ * Supported: dtype KVSS_BF16 or KVSS_F32; head_dim 64 or 128; block_size a multiple of 16.
+ */
+typedef struct kvss_kv {
+    const void* k;
+    const void* v;
+    const int32_t* block_table;
+    const int32_t* kv_lens;
+    int32_t batch;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t max_blocks;
+    int32_t num_blocks;
+    int32_t max_kv_len;
+    int32_t dtype;
+} kvss_kv;
+
+/* Thread-local description of the last error (empty string after success). */
+KVSS_API const char* kvss_last_error(void);
+
+/* Library ABI version (increments on any signature or semantic change). */
+KVSS_API int kvss_version(void);
+
+/*
+ * verify_attn_full -- T = gamma + 1 causal queries per sequence over the full cache.
+ * MagicDec Section 3.1 (T_V(B,S,gamma), Eq. (2)) and Section 3.2: verification reads the same
+ * KV cache as plain decoding, which is what makes it cheap in the long-context regime.
+ *   q    [batch, num_q_heads, T, head_dim] of kv->dtype. Query t of sequence b sits at
+ *        position kv_lens[b] - T + t (the T new rows are already in the cache) and attends to
+ *        rows [0, kv_lens[b] - T + t]; q-head h reads KV head h / G, G = num_q_heads /
+ *        num_kv_heads. A query with an empty range yields out = 0, lse = -inf.
+ *   out  float32 [batch, num_q_heads, T, head_dim]: softmax(scale * q K^T) V.
+ *   lse  float32 [batch, num_q_heads, T] or NULL: natural-log sum of exp(scale * q k).
+ * Limits: G * T <= 32.
+ */
+KVSS_API size_t kvss_verify_workspace_bytes(const kvss_kv* kv, int num_q_heads, int T);
+KVSS_API int verify_attn_full(const kvss_kv* kv, const void* q, int num_q_heads, int T, float scale,
+                     float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * draft_attn_sparse -- one draft query per sequence over a sparse subset of the cache.
+ * MagicDec Section 4.1, Eq. (3) (T_D(B,K): decoding against K selected rows) and Appendix A.1,
+ * Fig. 8 (self-speculation drafts from a compressed view of the target's own cache).
+ *   q         [batch, num_q_heads, head_dim] of kv->dtype.
+ *   sel_idx   int32 [batch, num_kv_heads, k_max]: selected positions, ascending, each in
+ *             [0, tail_lo[b]); entries i >= sel_count[b] are ignored. Entries outside
+ *             [0, min(tail_lo[b], kv_lens[b])) are skipped. May be NULL when k_max == 0.
+ *   sel_count int32 [batch] (may be NULL when k_max == 0).
+ *   tail_lo   int32 [batch]: the dense tail [tail_lo[b], kv_lens[b]) is attended as well.
+ *   max_tail  host-side estimate of max_b (kv_lens[b] - tail_lo[b]); it only shapes the launch
+ *             (the whole set is attended whatever the actual tail length).
+ *   out       float32 [batch, num_q_heads, head_dim]; lse float32 [batch, num_q_heads] or NULL.
+ * Limits: G <= 32, k_max >= 0, max_tail >= 0.
+ */
+KVSS_API size_t kvss_draft_workspace_bytes(const kvss_kv* kv, int num_q_heads, int k_max, int max_tail);
+KVSS_API int draft_attn_sparse(const kvss_kv* kv, const void* q, int num_q_heads,
+                      const int32_t* sel_idx, const int32_t* sel_count, int k_max,
+                      const int32_t* tail_lo, int max_tail, float scale, float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvss_streaming_set -- StreamingLLM draft set in the draft_attn_sparse encoding.
+ * MagicDec Section 5.1 (StreamingLLM-style sparse KV drafting) and Table 1 (budget 512).
+ * For L = kv_lens[b]: sel_idx[b, g, j] = j for j < min(sink, L), else -1 (j < sink);
+ * sel_count[b] = min(sink, L); tail_lo[b] = max(sink, L - window). The attended set is the
+ * first `sink` rows plus the last `window` rows (the current token included).
+ *   sel_idx int32 [batch, num_kv_heads, sink]; sel_count, tail_lo int32 [batch].
+ */
+KVSS_API int kvss_streaming_set(const int32_t* kv_lens, int batch, int num_kv_heads, int sink,
+                       int window, int32_t* sel_idx, int32_t* sel_count, int32_t* tail_lo,
+                       void* stream);
+
+/*
+ * snapkv_select -- static SnapKV selection of the draft cache from the prompt.
+ * MagicDec Section 4.4 (static selection: no per-query search cost), Section 5.2 (SnapKV
+ * budgets) and Appendix A.1 (built during prefill). For sequence b with P = kv_lens[b] prompt
+ * rows, q-head h of group g and observation query i < w at position P - w + i:
+ *   1. softmax of scale * q k over keys [0, P - w + i];
+ *   2. c[b, g, j] = sum over h in g, i < w of those probabilities, j in [0, P - w);
+ *   3. pooled = centred max-pool of width pool_kernel (odd) over [0, P - w);
+ *   4. keep the k = budget - w largest pooled values (ties: lower position), ascending.
+ *   q_obs      [batch, num_q_heads, w, head_dim] of kv->dtype.
+ *   sel_idx    int32 [batch, num_kv_heads, budget - w], -1 padded.
+ *   sel_count  int32 [batch] = min(budget - w, max(P - w, 0)).
+ *   scores_out float32 [batch, num_kv_heads, max_kv_len - w] or NULL: the column scores c
+ *              (entries j >= P - w of a shorter prompt are left untouched).
+ * The draft then attends sel_idx plus the dense tail [P - w, L).
+ * Limits: 0 < w < budget, G * w <= 256, pool_kernel odd and >= 1.
+ */
+KVSS_API size_t kvss_snapkv_workspace_bytes(const kvss_kv* kv, int num_q_heads, int w, int budget);
+KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads, int w, int pool_kernel,
+                  int budget, float scale, int32_t* sel_idx, int32_t* sel_count,
+                  float* scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_accept -- acceptance of gamma draft tokens against gamma + 1 target positions.
+ * MagicDec Section 3.1 (speculative decoding of Leviathan et al.; Eq. (1) gives the expected
+ * number of emitted tokens) and Section 5.1 (greedy decoding in all end-to-end runs).
+ *   target_logits float32 [batch, gamma + 1, vocab]; draft_logits float32 [batch, gamma,
+ *   vocab] (not read when temperature == 0; may then be NULL); draft_tokens int32
+ *   [batch, gamma], each in [0, vocab).
+ *   temperature == 0: greedy. Draft token i is accepted while it equals the target argmax at
+ *     position i (ties: lowest id); the first mismatch emits the target argmax there; if all
+ *     match, the argmax at position gamma is appended.
+ *   temperature > 0: rejection sampling with p = softmax(target / temperature), q = softmax(
+ *     draft / temperature). Position i accepts when u_i < p_i(x_i) / q_i(x_i); the first
+ *     rejection emits a draw from max(0, p_i - q_i) (from p_i if that is all zero); if all are
+ *     accepted a draw from p_gamma is appended. Draws are exponential races,
+ *     argmin_x -log(u'_x) / w(x). Uniforms come from Philox4x32-10 (Salmon et al., SC'11) with
+ *     key (seed low, seed high) and counter (block j, stream << 16 | position, b,
+ *     offset low 32 bits); stream 0 word 0 gives u_i, stream 1 word x % 4 of block x / 4
+ *     gives u'_x; a 32-bit word x maps to (x >> 9) * 2^-23 + 2^-24. Callers advance `offset`
+ *     between calls that share a seed.
+ *   out_tokens       int32 [batch, gamma + 1]: emitted tokens, then -1.
+ *   out_num_accepted int32 [batch]: accepted draft tokens, 0 .. gamma.
+ *   row_stats        float32 [batch, 2 * gamma + 1, 4] or NULL: per logit row (target rows
+ *                    0..gamma, then draft rows 0..gamma-1) the max of z / temperature, the sum
+ *                    of exp(z / temperature - max), z / temperature at the row's draft token
+ *                    (0 for the last target row), and the argmax as a float. With
+ *                    temperature == 0 only the argmax of target rows is filled (others 0).
+ */
+KVSS_API size_t kvss_accept_workspace_bytes(int batch, int gamma, int vocab);
+KVSS_API int spec_accept(const float* target_logits, const float* draft_logits,
+                const int32_t* draft_tokens, int batch, int gamma, int vocab, float temperature,
+                uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
+                float* row_stats, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSS_H */

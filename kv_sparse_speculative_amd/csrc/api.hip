@@ -1,0 +1,362 @@
+// C ABI of libkvss: argument validation (host only, before any HIP call), launch planning,
+// workspace carving and error reporting. The operations are declared and specified in
+// include/kvss.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kvss.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return KVSS_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(KVSS_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+// Workgroups a launch should offer: 256 compute units, a few resident workgroups each.
+constexpr long kTargetWorkgroups = 1024;
+constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes per round
+constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
+
+struct Plan {
+    int nsplit;
+    int split_len;
+};
+
+// Split a virtual key range of up to max_total keys per (sequence, KV head) so that the
+// launch offers about kTargetWorkgroups workgroups, each doing at least four rounds.
+Plan plan_splits(long pairs, long max_total, int unit) {
+    Plan p{1, unit};
+    if (max_total <= 0 || pairs <= 0) return p;
+    const long want = ceil_div(kTargetWorkgroups, pairs);
+    const long useful = ceil_div(max_total, 4L * unit);
+    long ns = want < useful ? want : useful;
+    if (ns < 1) ns = 1;
+    const long len = ceil_div(ceil_div(max_total, ns), unit) * unit;
+    p.split_len = (int)len;
+    p.nsplit = (int)ceil_div(max_total, len);
+    return p;
+}
+
+int check_kv(const kvss_kv* kv) {
+    if (!kv) return fail(KVSS_EINVAL, "kv descriptor is NULL");
+    if (kv->batch < 0) return fail(KVSS_EINVAL, "batch must be >= 0 (got %d)", kv->batch);
+    if (kv->dtype != KVSS_F32 && kv->dtype != KVSS_BF16)
+        return fail(KVSS_EUNSUPPORTED, "dtype %d is not KVSS_F32 or KVSS_BF16", kv->dtype);
+    if (kv->head_dim != 64 && kv->head_dim != 128)
+        return fail(KVSS_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", kv->head_dim);
+    if (kv->block_size <= 0 || kv->block_size % 16 != 0)
+        return fail(KVSS_EUNSUPPORTED, "block_size %d is not a positive multiple of 16", kv->block_size);
+    if (kv->num_kv_heads <= 0) return fail(KVSS_EINVAL, "num_kv_heads must be >= 1");
+    if (kv->max_kv_len < 0) return fail(KVSS_EINVAL, "max_kv_len must be >= 0");
+    if (kv->batch == 0) return ok();
+    if (kv->max_blocks <= 0 || kv->num_blocks <= 0)
+        return fail(KVSS_EINVAL, "max_blocks and num_blocks must be >= 1");
+    if ((long)kv->max_kv_len > (long)kv->max_blocks * kv->block_size)
+        return fail(KVSS_EINVAL, "max_kv_len %d exceeds max_blocks * block_size = %ld", kv->max_kv_len,
+                    (long)kv->max_blocks * kv->block_size);
+    if (!kv->k || !kv->v || !kv->block_table || !kv->kv_lens)
+        return fail(KVSS_EINVAL, "kv tensors (k, v, block_table, kv_lens) must be non-NULL");
+    return ok();
+}
+
+kvss::AttnArgs attn_common(const kvss_kv* kv) {
+    kvss::AttnArgs a{};
+    a.k = kv->k;
+    a.v = kv->v;
+    a.block_table = kv->block_table;
+    a.kv_lens = kv->kv_lens;
+    a.B = kv->batch;
+    a.Hkv = kv->num_kv_heads;
+    a.D = kv->head_dim;
+    a.bs = kv->block_size;
+    a.max_blocks = kv->max_blocks;
+    a.num_blocks = kv->num_blocks;
+    a.max_kv_len = kv->max_kv_len;
+    return a;
+}
+
+float scale_log2(float scale) { return (float)((double)scale * 1.4426950408889634); }
+
+Plan verify_plan(const kvss_kv* kv) {
+    return plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len,
+                       kv->dtype == KVSS_BF16 ? kMfmaUnit : kSimpleUnit);
+}
+
+size_t partial_bytes(long rows, const Plan& p, int D) {
+    return p.nsplit > 1 ? align_up((size_t)rows * p.nsplit * (D + 2) * sizeof(float)) : 0;
+}
+
+int check_heads(const kvss_kv* kv, int num_q_heads) {
+    if (num_q_heads <= 0 || num_q_heads % kv->num_kv_heads != 0)
+        return fail(KVSS_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                    num_q_heads, kv->num_kv_heads);
+    return ok();
+}
+
+int run_attention(kvss::AttnArgs& a, const Plan& p, bool gather, int dtype, void* ws,
+                  hipStream_t s) {
+    a.nsplit = p.nsplit;
+    a.split_len = p.split_len;
+    a.part = p.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
+    hipError_t e = dtype == KVSS_BF16 ? kvss::launch_attn_mfma(a, gather, s)
+                                      : kvss::launch_attn_simple(a, gather, s);
+    if (e != hipSuccess) return hip_status(e, "attention launch");
+    if (p.nsplit > 1) {
+        e = kvss::launch_merge(a.part, a.B * a.Hq * a.T, p.nsplit, a.D, a.out, a.lse, s);
+        if (e != hipSuccess) return hip_status(e, "split merge launch");
+    }
+    return ok();
+}
+
+struct SnapLayout {
+    Plan p1;
+    int R, n_stride;
+    size_t part1, scores, pooled, total;
+};
+
+SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_scores) {
+    SnapLayout s{};
+    const int G = num_q_heads / kv->num_kv_heads;
+    s.R = G * w;
+    s.p1 = plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kSimpleUnit);
+    s.n_stride = kv->max_kv_len > w ? kv->max_kv_len - w : 0;
+    const size_t rows = (size_t)kv->batch * kv->num_kv_heads;
+    s.part1 = align_up(rows * s.R * s.p1.nsplit * 2 * sizeof(float));
+    s.scores = own_scores ? align_up(rows * s.n_stride * sizeof(float)) : 0;
+    s.pooled = align_up(rows * s.n_stride * sizeof(float));
+    s.total = s.part1 + s.scores + s.pooled;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvss_last_error(void) { return g_err.c_str(); }
+
+int kvss_version(void) { return 1; }
+
+size_t kvss_verify_workspace_bytes(const kvss_kv* kv, int num_q_heads, int T) {
+    if (check_kv(kv) != KVSS_OK || num_q_heads <= 0 || T <= 0) return 0;
+    return partial_bytes((long)kv->batch * num_q_heads * T, verify_plan(kv), kv->head_dim);
+}
+
+int verify_attn_full(const kvss_kv* kv, const void* q, int num_q_heads, int T, float scale,
+                     float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    int rc = check_kv(kv);
+    if (rc) return rc;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (T <= 0) return fail(KVSS_EINVAL, "T (gamma + 1) must be >= 1 (got %d)", T);
+    const int G = num_q_heads / kv->num_kv_heads;
+    if (G * T > 32) return fail(KVSS_EUNSUPPORTED, "G * T = %d exceeds 32 query rows per KV head", G * T);
+    if (!isfinite(scale)) return fail(KVSS_EINVAL, "scale must be finite");
+    if (kv->batch == 0) return ok();
+    if (!q || !out) return fail(KVSS_EINVAL, "q and out must be non-NULL");
+    const Plan p = verify_plan(kv);
+    const size_t need = partial_bytes((long)kv->batch * num_q_heads * T, p, kv->head_dim);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
+    kvss::AttnArgs a = attn_common(kv);
+    a.q = q;
+    a.Hq = num_q_heads;
+    a.G = G;
+    a.T = T;
+    a.R = G * T;
+    a.scale_log2 = scale_log2(scale);
+    a.out = out;
+    a.lse = lse;
+    return run_attention(a, p, false, kv->dtype, workspace, static_cast<hipStream_t>(stream));
+}
+
+static Plan draft_plan(const kvss_kv* kv, int k_max, int max_tail) {
+    return plan_splits((long)kv->batch * kv->num_kv_heads, (long)k_max + max_tail,
+                       kv->dtype == KVSS_BF16 ? kMfmaUnit : kSimpleUnit);
+}
+
+size_t kvss_draft_workspace_bytes(const kvss_kv* kv, int num_q_heads, int k_max, int max_tail) {
+    if (check_kv(kv) != KVSS_OK || num_q_heads <= 0 || k_max < 0 || max_tail < 0) return 0;
+    return partial_bytes((long)kv->batch * num_q_heads, draft_plan(kv, k_max, max_tail),
+                         kv->head_dim);
+}
+
+int draft_attn_sparse(const kvss_kv* kv, const void* q, int num_q_heads, const int32_t* sel_idx,
+                      const int32_t* sel_count, int k_max, const int32_t* tail_lo, int max_tail,
+                      float scale, float* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int rc = check_kv(kv);
+    if (rc) return rc;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    const int G = num_q_heads / kv->num_kv_heads;
+    if (G > 32) return fail(KVSS_EUNSUPPORTED, "G = %d exceeds 32 query rows per KV head", G);
+    if (k_max < 0) return fail(KVSS_EINVAL, "k_max must be >= 0");
+    if (max_tail < 0) return fail(KVSS_EINVAL, "max_tail must be >= 0");
+    if (!isfinite(scale)) return fail(KVSS_EINVAL, "scale must be finite");
+    if (kv->batch == 0) return ok();
+    if (!q || !out || !tail_lo) return fail(KVSS_EINVAL, "q, out and tail_lo must be non-NULL");
+    if (k_max > 0 && (!sel_idx || !sel_count))
+        return fail(KVSS_EINVAL, "sel_idx and sel_count must be non-NULL when k_max > 0");
+    const Plan p = draft_plan(kv, k_max, max_tail);
+    const size_t need = partial_bytes((long)kv->batch * num_q_heads, p, kv->head_dim);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
+    static const int32_t* const kNoList = nullptr;
+    kvss::AttnArgs a = attn_common(kv);
+    a.q = q;
+    a.Hq = num_q_heads;
+    a.G = G;
+    a.T = 1;
+    a.R = G;
+    a.sel_idx = k_max > 0 ? sel_idx : kNoList;
+    a.sel_count = sel_count;
+    a.tail_lo = tail_lo;
+    a.k_max = k_max;
+    if (k_max == 0) a.sel_count = tail_lo;   // read but clamped to k_max = 0
+    a.scale_log2 = scale_log2(scale);
+    a.out = out;
+    a.lse = lse;
+    return run_attention(a, p, true, kv->dtype, workspace, static_cast<hipStream_t>(stream));
+}
+
+int kvss_streaming_set(const int32_t* kv_lens, int batch, int num_kv_heads, int sink, int window,
+                       int32_t* sel_idx, int32_t* sel_count, int32_t* tail_lo, void* stream) {
+    if (batch < 0 || num_kv_heads <= 0 || sink < 0 || window < 0)
+        return fail(KVSS_EINVAL, "batch, sink, window must be >= 0 and num_kv_heads >= 1");
+    if (batch == 0) return ok();
+    if (!kv_lens || !sel_count || !tail_lo || (sink > 0 && !sel_idx))
+        return fail(KVSS_EINVAL, "kv_lens, sel_idx, sel_count and tail_lo must be non-NULL");
+    return hip_status(kvss::launch_streaming_set(kv_lens, batch, num_kv_heads, sink, window, sel_idx,
+                                                 sel_count, tail_lo, static_cast<hipStream_t>(stream)),
+                      "streaming set launch");
+}
+
+size_t kvss_snapkv_workspace_bytes(const kvss_kv* kv, int num_q_heads, int w, int budget) {
+    if (check_kv(kv) != KVSS_OK || num_q_heads <= 0 || num_q_heads % kv->num_kv_heads || w <= 0 ||
+        budget <= w)
+        return 0;
+    return snap_layout(kv, num_q_heads, w, true).total;
+}
+
+int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads, int w, int pool_kernel,
+                  int budget, float scale, int32_t* sel_idx, int32_t* sel_count,
+                  float* scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_kv(kv);
+    if (rc) return rc;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (w <= 0) return fail(KVSS_EINVAL, "observation window w must be >= 1");
+    if (budget <= w) return fail(KVSS_EINVAL, "budget %d must exceed the window %d", budget, w);
+    if (pool_kernel < 1 || pool_kernel % 2 == 0)
+        return fail(KVSS_EINVAL, "pool_kernel %d must be odd and >= 1", pool_kernel);
+    const int G = num_q_heads / kv->num_kv_heads;
+    if (G * w > 256) return fail(KVSS_EUNSUPPORTED, "G * w = %d exceeds 256 rows per KV head", G * w);
+    if (!isfinite(scale)) return fail(KVSS_EINVAL, "scale must be finite");
+    if (kv->batch == 0) return ok();
+    if (!q_obs || !sel_idx || !sel_count)
+        return fail(KVSS_EINVAL, "q_obs, sel_idx and sel_count must be non-NULL");
+    // The full requirement (workspace holds the scores too) is what the query reports; when the
+    // caller keeps the scores, less is needed.
+    const SnapLayout L = snap_layout(kv, num_q_heads, w, scores_out == nullptr);
+    if (workspace_bytes < L.total || (L.total > 0 && !workspace))
+        return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, L.total);
+    char* ws = static_cast<char*>(workspace);
+    kvss::SnapArgs a{};
+    a.k = kv->k;
+    a.block_table = kv->block_table;
+    a.prompt_lens = kv->kv_lens;
+    a.B = kv->batch;
+    a.Hkv = kv->num_kv_heads;
+    a.D = kv->head_dim;
+    a.bs = kv->block_size;
+    a.max_blocks = kv->max_blocks;
+    a.num_blocks = kv->num_blocks;
+    a.max_kv_len = kv->max_kv_len;
+    a.dtype = kv->dtype;
+    a.q_obs = q_obs;
+    a.Hq = num_q_heads;
+    a.G = G;
+    a.w = w;
+    a.R = G * w;
+    a.scale_log2 = scale_log2(scale);
+    a.nsplit1 = L.p1.nsplit;
+    a.split_len1 = L.p1.split_len;
+    a.part1 = reinterpret_cast<float*>(ws);
+    a.scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + L.part1);
+    a.n_stride = L.n_stride;
+    a.pooled = reinterpret_cast<float*>(ws + L.part1 + L.scores);
+    a.pool = pool_kernel;
+    a.keep = budget - w;
+    a.sel_idx = sel_idx;
+    a.sel_count = sel_count;
+    return hip_status(kvss::launch_snapkv(a, static_cast<hipStream_t>(stream)), "snapkv launch");
+}
+
+size_t kvss_accept_workspace_bytes(int batch, int gamma, int vocab) {
+    if (batch < 0 || gamma < 0 || vocab <= 0) return 0;
+    return align_up((size_t)batch * (2 * gamma + 1) * 4 * sizeof(float));
+}
+
+int spec_accept(const float* target_logits, const float* draft_logits, const int32_t* draft_tokens,
+                int batch, int gamma, int vocab, float temperature, uint64_t seed, uint64_t offset,
+                int32_t* out_tokens, int32_t* out_num_accepted, float* row_stats, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (batch < 0) return fail(KVSS_EINVAL, "batch must be >= 0");
+    if (gamma < 0 || gamma >= 65536) return fail(KVSS_EINVAL, "gamma must be in [0, 65536)");
+    if (vocab <= 0 || vocab >= (1 << 24)) return fail(KVSS_EINVAL, "vocab must be in [1, 2^24)");
+    if (!(temperature >= 0.f) || !isfinite(temperature))
+        return fail(KVSS_EINVAL, "temperature must be finite and >= 0");
+    if (batch == 0) return ok();
+    if (!target_logits || !out_tokens || !out_num_accepted || (gamma > 0 && !draft_tokens))
+        return fail(KVSS_EINVAL, "target_logits, draft_tokens, out_tokens, out_num_accepted must be non-NULL");
+    if (temperature > 0.f && gamma > 0 && !draft_logits)
+        return fail(KVSS_EINVAL, "draft_logits must be non-NULL when temperature > 0");
+    const size_t need = row_stats ? 0 : kvss_accept_workspace_bytes(batch, gamma, vocab);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
+    kvss::AcceptArgs a{};
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.tokens = draft_tokens;
+    a.B = batch;
+    a.gamma = gamma;
+    a.V = vocab;
+    a.inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
+    a.seed = seed;
+    a.offset = offset;
+    a.stats = row_stats ? row_stats : static_cast<float*>(workspace);
+    a.out_tokens = out_tokens;
+    a.out_num = out_num_accepted;
+    return hip_status(kvss::launch_accept(a, static_cast<hipStream_t>(stream)), "accept launch");
+}
+
+}  // extern "C"

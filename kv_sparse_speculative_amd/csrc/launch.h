@@ -1,0 +1,73 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvss {
+
+// One attention launch: R = G * T query rows per (sequence, KV head) over a key set that is
+// either the dense causal range [0, L) (verify) or a gathered list + dense tail (draft).
+struct AttnArgs {
+    const void* k;
+    const void* v;
+    const int32_t* block_table;
+    const int32_t* kv_lens;
+    int B, Hkv, D, bs, max_blocks, num_blocks, max_kv_len;
+    const void* q;              // [B, Hq, T, D]
+    int Hq, G, T, R;
+    const int32_t* sel_idx;     // gather mode only: [B, Hkv, k_max]
+    const int32_t* sel_count;   // [B]
+    const int32_t* tail_lo;     // [B]
+    int k_max;
+    float scale_log2;           // softmax scale * log2(e)
+    int nsplit, split_len;      // virtual key range of split s: [s*split_len, (s+1)*split_len)
+    float* out;                 // [B, Hq, T, D]
+    float* lse;                 // [B, Hq, T] or null
+    float* part;                // [B*Hq*T, nsplit, D + 2] when nsplit > 1
+};
+
+hipError_t launch_attn_mfma(const AttnArgs& a, bool gather, hipStream_t s);
+hipError_t launch_attn_simple(const AttnArgs& a, bool gather, hipStream_t s);
+hipError_t launch_merge(const float* part, int rows, int nsplit, int D, float* out, float* lse,
+                        hipStream_t s);
+
+struct SnapArgs {
+    const void* k;
+    const int32_t* block_table;
+    const int32_t* prompt_lens;
+    int B, Hkv, D, bs, max_blocks, num_blocks, max_kv_len, dtype;
+    const void* q_obs;          // [B, Hq, w, D]
+    int Hq, G, w, R;            // R = G * w rows per (sequence, KV head)
+    float scale_log2;
+    int nsplit1, split_len1;    // pass-1 key splits
+    float* part1;               // [B*Hkv*R, nsplit1, 2] row (max, sum) partials, log2 domain
+    float* scores;              // [B, Hkv, n_stride] column scores
+    int n_stride;               // max_kv_len - w
+    float* pooled;              // [B, Hkv, n_stride] workspace
+    int pool, keep;             // pool kernel, kept count budget - w
+    int32_t* sel_idx;           // [B, Hkv, keep]
+    int32_t* sel_count;         // [B]
+};
+
+hipError_t launch_snapkv(const SnapArgs& a, hipStream_t s);
+
+hipError_t launch_streaming_set(const int32_t* kv_lens, int B, int Hkv, int sink, int window,
+                                int32_t* sel_idx, int32_t* sel_count, int32_t* tail_lo,
+                                hipStream_t s);
+
+struct AcceptArgs {
+    const float* target;        // [B, gamma+1, V]
+    const float* draft;         // [B, gamma, V]
+    const int32_t* tokens;      // [B, gamma]
+    int B, gamma, V;
+    float inv_temp;             // 0 => greedy
+    uint64_t seed, offset;
+    float* stats;               // [B, 2*gamma+1, 4]
+    int32_t* out_tokens;        // [B, gamma+1]
+    int32_t* out_num;           // [B]
+};
+
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
+
+}  // namespace kvss

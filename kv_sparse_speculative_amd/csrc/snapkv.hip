@@ -1,0 +1,270 @@
+// SnapKV selection of the static draft cache (MagicDec Section 4.4: static KV selection,
+// computed once at prefill per Appendix A.1 / Fig. 8; budgets in Section 5.2).
+//
+// Three kernels:
+//   rowstats : per observation row (q-head h of group g, window query i) the softmax max and
+//              sum over its causal key range [0, P - w + i], split over key ranges;
+//   colscore : per candidate key j < P - w, c[j] = sum over the G * w rows of
+//              exp(s_rj - m_r) / l_r, with the row statistics merged from the splits;
+//   topk     : centred max-pool of c, then an exact radix select of the k-th largest pooled
+//              value on its IEEE bit pattern (scores are >= +0, so the bits order like the
+//              values) and an ordered compaction (ties go to the lower position), giving the
+//              kept positions in ascending order.
+// The score passes run on the vector ALU with the queries staged in LDS; they are
+// bit-deterministic (fixed key order per thread, no atomics on floats).
+
+#include "common.h"
+#include "launch.h"
+
+namespace kvss {
+namespace {
+
+template <typename ST>
+__device__ __forceinline__ float load_elem(const ST* p, size_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+template <typename ST, int D>
+__global__ __launch_bounds__(256) void snap_rowstats_kernel(SnapArgs a) {
+    __shared__ float kt[32][D + 1];
+    __shared__ long long soff[32];
+    __shared__ int sok[32];
+    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
+    const int begin = split * a.split_len1;
+    const int end = (split == a.nsplit1 - 1) ? P : min(begin + a.split_len1, P);
+    const PagedCache cache{a.block_table, a.Hkv, a.bs, a.max_blocks, a.num_blocks, D};
+    const ST* kp = static_cast<const ST*>(a.k);
+    const ST* qp = static_cast<const ST*>(a.q_obs);
+
+    const bool row_ok = tid < a.R;
+    const int h = g * a.G + (row_ok ? tid / a.w : 0), i = row_ok ? tid % a.w : 0;
+    const int limit = P - a.w + i;
+    float q[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        q[d] = row_ok ? load_elem(qp, (((size_t)b * a.Hq + h) * a.w + i) * D + d) : 0.f;
+    float m = kNegInf, l = 0.f;
+    bool bad = false;
+
+    for (int c0 = begin; c0 < end; c0 += 32) {
+        if (tid < 32) {
+            const int pos = c0 + tid;
+            bool ok = pos < end;
+            size_t off = 0;
+            if (ok && !cache.row_offset(b, g, pos, off)) { bad = true; ok = false; }
+            sok[tid] = ok;
+            soff[tid] = (long long)off;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < 32 * D; idx += 256) {
+            const int j = idx / D, d = idx % D;
+            kt[j][d] = sok[j] ? load_elem(kp, (size_t)soff[j] + d) : 0.f;
+        }
+        __syncthreads();
+        if (row_ok) {
+            for (int j = 0; j < 32; ++j) {
+                const int pos = c0 + j;
+                if (!sok[j] || pos > limit) continue;
+                float s = 0.f;
+#pragma unroll
+                for (int d = 0; d < D; ++d) s = fmaf(q[d], kt[j][d], s);
+                s *= a.scale_log2;
+                const float mnew = fmaxf(m, s);
+                l = l * __builtin_amdgcn_exp2f(m - mnew) + __builtin_amdgcn_exp2f(s - mnew);
+                m = mnew;
+            }
+        }
+        __syncthreads();
+    }
+    const bool poisoned = __syncthreads_or(bad);
+    if (row_ok) {
+        float* pp = a.part1 + ((((size_t)b * a.Hkv + g) * a.R + tid) * a.nsplit1 + split) * 2;
+        pp[0] = poisoned ? __builtin_nanf("") : m;
+        pp[1] = poisoned ? __builtin_nanf("") : l;
+    }
+}
+
+// Rows of the observation window staged in LDS at a time.
+template <typename ST>
+struct RowChunk { static constexpr int value = sizeof(ST) == 2 ? 128 : 64; };
+
+template <typename ST, int D>
+__global__ __launch_bounds__(256) void snap_colscore_kernel(SnapArgs a) {
+    constexpr int RC = RowChunk<ST>::value;
+    __shared__ __attribute__((aligned(16))) ST qs[RC * D];
+    __shared__ float rowc[256];
+    const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
+    const int n = max(P - a.w, 0);
+    const int j0 = tile * 256;
+    if (j0 >= n) return;
+    const ST* qp = static_cast<const ST*>(a.q_obs);
+
+    for (int r = tid; r < a.R; r += 256) {
+        const float* pp = a.part1 + (((size_t)b * a.Hkv + g) * a.R + r) * a.nsplit1 * 2;
+        float M = kNegInf;
+        bool nan = false;
+        for (int s = 0; s < a.nsplit1; ++s) { nan |= pp[2 * s] != pp[2 * s]; M = fmaxf(M, pp[2 * s]); }
+        float lam = 0.f;
+        if (M != kNegInf)
+            for (int s = 0; s < a.nsplit1; ++s)
+                if (pp[2 * s] != kNegInf) lam += __builtin_amdgcn_exp2f(pp[2 * s] - M) * pp[2 * s + 1];
+        // log2 of the row normaliser; rows with no visible key contribute nothing.
+        rowc[r] = nan ? __builtin_nanf("") : (lam > 0.f ? M + __log2f(lam) : __builtin_huge_valf());
+    }
+
+    const int j = j0 + tid;
+    const PagedCache cache{a.block_table, a.Hkv, a.bs, a.max_blocks, a.num_blocks, D};
+    size_t off = 0;
+    const bool live = j < n;
+    const bool ok = live && cache.row_offset(b, g, j, off);
+    const ST* kp = static_cast<const ST*>(a.k);
+    float kr[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) kr[d] = ok ? load_elem(kp, off + d) : 0.f;
+    float c = 0.f;
+    for (int r0 = 0; r0 < a.R; r0 += RC) {
+        const int rn = min(RC, a.R - r0);
+        __syncthreads();
+        for (int idx = tid; idx < rn * D; idx += 256) {
+            const int r = r0 + idx / D, d = idx % D;
+            const int h = g * a.G + r / a.w, i = r % a.w;
+            qs[idx] = qp[(((size_t)b * a.Hq + h) * a.w + i) * D + d];
+        }
+        __syncthreads();
+        for (int rr = 0; rr < rn; ++rr) {
+            const ST* qr = qs + (size_t)rr * D;
+            float s = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) s = fmaf(load_elem(qr, d), kr[d], s);
+            c += __builtin_amdgcn_exp2f(s * a.scale_log2 - rowc[r0 + rr]);
+        }
+    }
+    if (live) a.scores[((size_t)b * a.Hkv + g) * a.n_stride + j] = ok ? c : __builtin_nanf("");
+}
+
+// Exclusive prefix sum over the 1024 threads of a workgroup; also returns the total.
+__device__ int block_scan_1024(int v, int* sh, int& total) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[wid] = x;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int w = 0; w < 16; ++w) { run += sh[w]; sh[w] = run; }
+    }
+    __syncthreads();
+    const int base = wid > 0 ? sh[wid - 1] : 0;
+    total = sh[15];
+    __syncthreads();
+    return base + x - v;
+}
+
+__global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
+    __shared__ unsigned hist[256];
+    __shared__ int sh[16];
+    __shared__ unsigned s_digit, s_remaining;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
+    const int n = max(P - a.w, 0);
+    const int k = a.keep;
+    if (g == 0 && tid == 0) a.sel_count[b] = min(k, n);
+    int32_t* out = a.sel_idx + ((size_t)b * a.Hkv + g) * k;
+    if (n <= k) {
+        for (int j = tid; j < k; j += 1024) out[j] = j < n ? j : -1;
+        return;
+    }
+    const float* c = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
+    unsigned* pl = reinterpret_cast<unsigned*>(a.pooled + ((size_t)b * a.Hkv + g) * a.n_stride);
+    const int r = a.pool / 2;
+    for (int j = tid; j < n; j += 1024) {
+        float m = c[j];
+        for (int d = 1; d <= r; ++d) {
+            if (j - d >= 0) m = fmaxf(m, c[j - d]);
+            if (j + d < n) m = fmaxf(m, c[j + d]);
+        }
+        pl[j] = __float_as_uint(m);
+    }
+    __syncthreads();
+
+    // Radix select (most significant byte first) of the k-th largest bit pattern.
+    unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int t = tid; t < 256; t += 1024) hist[t] = 0;
+        __syncthreads();
+        for (int j = tid; j < n; j += 1024) {
+            const unsigned u = pl[j];
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            unsigned cum = 0;
+            for (int d = 255; d >= 0; --d) {
+                if (cum + hist[d] >= remaining) { s_digit = d; s_remaining = remaining - cum; break; }
+                cum += hist[d];
+            }
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        mask |= 255u << shift;
+        remaining = s_remaining;
+        __syncthreads();
+    }
+    const unsigned thr = prefix;     // k-th largest; `remaining` copies of it are kept
+
+    const int chunk = (n + 1023) / 1024;
+    const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
+    int gt = 0, eq = 0;
+    for (int j = lo; j < hi; ++j) {
+        const unsigned u = pl[j];
+        gt += u > thr;
+        eq += u == thr;
+    }
+    int tot;
+    const int eq_before = block_scan_1024(eq, sh, tot);
+    int take = min(max((int)remaining - eq_before, 0), eq);
+    int pos = block_scan_1024(gt + take, sh, tot);
+    for (int j = lo; j < hi && pos < k; ++j) {
+        const unsigned u = pl[j];
+        if (u > thr) out[pos++] = j;
+        else if (u == thr && take > 0) { out[pos++] = j; --take; }
+    }
+}
+
+template <typename ST, int D>
+hipError_t launch_typed(const SnapArgs& a, hipStream_t s) {
+    snap_rowstats_kernel<ST, D><<<dim3(a.nsplit1, a.Hkv, a.B), 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.n_stride > 0) {
+        snap_colscore_kernel<ST, D><<<dim3((a.n_stride + 255) / 256, a.Hkv, a.B), 256, 0, s>>>(a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    snap_topk_kernel<<<dim3(a.Hkv, a.B), 1024, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_snapkv(const SnapArgs& a, hipStream_t s) {
+    if (a.dtype == 1) {
+        return a.D == 128 ? launch_typed<uint16_t, 128>(a, s) : launch_typed<uint16_t, 64>(a, s);
+    }
+    return a.D == 128 ? launch_typed<float, 128>(a, s) : launch_typed<float, 64>(a, s);
+}
+
+}  // namespace kvss

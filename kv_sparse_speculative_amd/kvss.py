@@ -1,0 +1,254 @@
+"""Thin Python binding of libkvss (include/kvss.h), same names as the C ABI.
+
+Argument marshalling only: tensors are checked for device, dtype and contiguity, their device
+pointers and torch's current HIP stream are handed to the library, and missing outputs or
+workspaces are allocated with torch. Every step of the computation runs in the library's HIP
+kernels; there is no fallback. Loading fails loudly if libkvss.so has not been built.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvss.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "kvss.h")
+
+KVSS_OK, KVSS_EINVAL, KVSS_EUNSUPPORTED, KVSS_EWORKSPACE, KVSS_EHIP = 0, -1, -2, -3, -4
+KVSS_F32, KVSS_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: KVSS_F32, torch.bfloat16: KVSS_BF16}
+
+
+class KvssError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"kvss error {code}: {message}")
+        self.code = code
+
+
+class kvss_kv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_kv_len", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+_U64 = ctypes.c_uint64
+_KV = ctypes.POINTER(kvss_kv)
+
+_SIGNATURES = {
+    "kvss_last_error": (ctypes.c_char_p, []),
+    "kvss_version": (_I, []),
+    "kvss_verify_workspace_bytes": (_Z, [_KV, _I, _I]),
+    "verify_attn_full": (_I, [_KV, _P, _I, _I, _F, _P, _P, _P, _Z, _P]),
+    "kvss_draft_workspace_bytes": (_Z, [_KV, _I, _I, _I]),
+    "draft_attn_sparse": (_I, [_KV, _P, _I, _P, _P, _I, _P, _I, _F, _P, _P, _P, _Z, _P]),
+    "kvss_streaming_set": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "kvss_snapkv_workspace_bytes": (_Z, [_KV, _I, _I, _I]),
+    "snapkv_select": (_I, [_KV, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _Z, _P]),
+    "kvss_accept_workspace_bytes": (_Z, [_I, _I, _I]),
+    "spec_accept": (_I, [_P, _P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _Z, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with kv_sparse_speculative_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def declared_functions():
+    """Function names declared with KVSS_API in include/kvss.h."""
+    text = open(HEADER).read()
+    return re.findall(r"KVSS_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def _check(rc):
+    if rc != KVSS_OK:
+        raise KvssError(rc, lib().kvss_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t, name, dtype=None, device=True):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+class PagedKV:
+    """A paged per-layer KV cache: k, v [num_blocks, Hkv, block_size, D] (bf16 or f32),
+    block_table int32 [B, max_blocks], kv_lens int32 [B] and a host bound max_kv_len."""
+
+    def __init__(self, k, v, block_table, kv_lens, max_kv_len):
+        for t, n in ((k, "k"), (v, "v")):
+            _need(t, n)
+        _need(block_table, "block_table", torch.int32)
+        _need(kv_lens, "kv_lens", torch.int32)
+        if k.dtype not in _DTYPE_CODE or v.dtype != k.dtype or v.shape != k.shape:
+            raise ValueError("k and v must share shape and a bf16 / f32 dtype")
+        self.k, self.v, self.block_table, self.kv_lens = k, v, block_table, kv_lens
+        self.max_kv_len = int(max_kv_len)
+        self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = k.shape
+        self.batch, self.max_blocks = block_table.shape
+        self.dtype = k.dtype
+
+    def with_lens(self, kv_lens, max_kv_len):
+        return PagedKV(self.k, self.v, self.block_table, kv_lens, max_kv_len)
+
+    def desc(self):
+        return kvss_kv(self.k.data_ptr(), self.v.data_ptr(), self.block_table.data_ptr(),
+                       self.kv_lens.data_ptr(), self.batch, self.num_kv_heads, self.head_dim,
+                       self.block_size, self.max_blocks, self.num_blocks, self.max_kv_len,
+                       _DTYPE_CODE[self.dtype])
+
+
+def _workspace(nbytes, workspace, device):
+    if nbytes == 0:
+        return workspace, 0 if workspace is None else workspace.numel()
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def verify_attn_full(kv, q, scale=None, out=None, lse=None, want_lse=True, workspace=None,
+                     stream=None):
+    """q [B, Hq, T, D] -> (out [B, Hq, T, D] f32, lse [B, Hq, T] f32 or None)."""
+    _need(q, "q", kv.dtype)
+    B, Hq, T, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, Hq, T, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    d = kv.desc()
+    nbytes = lib().kvss_verify_workspace_bytes(ctypes.byref(d), Hq, T)
+    workspace, wsb = _workspace(nbytes, workspace, q.device)
+    _check(lib().verify_attn_full(ctypes.byref(d), q.data_ptr(), Hq, T, scale, out.data_ptr(),
+                                  _ptr(lse), _ptr(workspace), wsb, _stream(stream)))
+    return out, lse
+
+
+def draft_attn_sparse(kv, q, sel_idx, sel_count, tail_lo, max_tail, scale=None, out=None,
+                      lse=None, want_lse=True, workspace=None, stream=None):
+    """q [B, Hq, D]; sel_idx int32 [B, Hkv, k_max]; sel_count, tail_lo int32 [B]."""
+    _need(q, "q", kv.dtype)
+    B, Hq, D = q.shape
+    k_max = 0 if sel_idx is None else sel_idx.shape[-1]
+    if sel_idx is not None:
+        _need(sel_idx, "sel_idx", torch.int32)
+        _need(sel_count, "sel_count", torch.int32)
+    _need(tail_lo, "tail_lo", torch.int32)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    d = kv.desc()
+    nbytes = lib().kvss_draft_workspace_bytes(ctypes.byref(d), Hq, k_max, int(max_tail))
+    workspace, wsb = _workspace(nbytes, workspace, q.device)
+    _check(lib().draft_attn_sparse(ctypes.byref(d), q.data_ptr(), Hq, _ptr(sel_idx),
+                                   _ptr(sel_count), k_max, tail_lo.data_ptr(), int(max_tail),
+                                   scale, out.data_ptr(), _ptr(lse), _ptr(workspace), wsb,
+                                   _stream(stream)))
+    return out, lse
+
+
+def kvss_streaming_set(kv_lens, num_kv_heads, sink, window, sel_idx=None, sel_count=None,
+                       tail_lo=None, stream=None):
+    """StreamingLLM set -> (sel_idx [B, Hkv, sink], sel_count [B], tail_lo [B]) int32."""
+    _need(kv_lens, "kv_lens", torch.int32)
+    B = kv_lens.shape[0]
+    dev = kv_lens.device
+    if sel_idx is None:
+        sel_idx = torch.empty((B, num_kv_heads, sink), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty(B, dtype=torch.int32, device=dev)
+    if tail_lo is None:
+        tail_lo = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib().kvss_streaming_set(kv_lens.data_ptr(), B, num_kv_heads, sink, window,
+                                    sel_idx.data_ptr(), sel_count.data_ptr(), tail_lo.data_ptr(),
+                                    _stream(stream)))
+    return sel_idx, sel_count, tail_lo
+
+
+def snapkv_select(kv, q_obs, w, pool_kernel, budget, scale=None, scores_out=None,
+                  want_scores=False, sel_idx=None, sel_count=None, workspace=None, stream=None):
+    """kv.kv_lens = prompt lengths; q_obs [B, Hq, w, D] -> (sel_idx, sel_count, scores|None)."""
+    _need(q_obs, "q_obs", kv.dtype)
+    B, Hq, w_, D = q_obs.shape
+    if w_ != w:
+        raise ValueError("q_obs window does not match w")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dev = q_obs.device
+    if sel_idx is None:
+        sel_idx = torch.empty((B, kv.num_kv_heads, budget - w), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty(B, dtype=torch.int32, device=dev)
+    if scores_out is None and want_scores:
+        scores_out = torch.zeros((B, kv.num_kv_heads, max(kv.max_kv_len - w, 0)),
+                                 dtype=torch.float32, device=dev)
+    d = kv.desc()
+    nbytes = lib().kvss_snapkv_workspace_bytes(ctypes.byref(d), Hq, w, budget)
+    workspace, wsb = _workspace(nbytes, workspace, dev)
+    _check(lib().snapkv_select(ctypes.byref(d), q_obs.data_ptr(), Hq, w, pool_kernel, budget,
+                               scale, sel_idx.data_ptr(), sel_count.data_ptr(), _ptr(scores_out),
+                               _ptr(workspace), wsb, _stream(stream)))
+    return sel_idx, sel_count, scores_out
+
+
+def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, offset=0,
+                row_stats=None, want_stats=False, out_tokens=None, num_accepted=None,
+                workspace=None, stream=None):
+    """target [B, gamma+1, V], draft [B, gamma, V] f32; tokens int32 [B, gamma]
+    -> (out_tokens [B, gamma+1], num_accepted [B], row_stats [B, 2gamma+1, 4] or None)."""
+    _need(target_logits, "target_logits", torch.float32)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32)
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    B, T, V = target_logits.shape
+    gamma = T - 1
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, T), dtype=torch.int32, device=dev)
+    n_acc = num_accepted
+    if n_acc is None:
+        n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    if row_stats is None and want_stats:
+        row_stats = torch.zeros((B, 2 * gamma + 1, 4), dtype=torch.float32, device=dev)
+    nbytes = 0 if row_stats is not None else lib().kvss_accept_workspace_bytes(B, gamma, V)
+    workspace, wsb = _workspace(nbytes, workspace, dev)
+    _check(lib().spec_accept(target_logits.data_ptr(), _ptr(draft_logits), draft_tokens.data_ptr(),
+                             B, gamma, V, float(temperature), int(seed) & (2**64 - 1),
+                             int(offset) & (2**64 - 1), out_tokens.data_ptr(), n_acc.data_ptr(),
+                             _ptr(row_stats), _ptr(workspace), wsb, _stream(stream)))
+    return out_tokens, n_acc, row_stats

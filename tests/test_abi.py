@@ -1,0 +1,112 @@
+"""CPU checks of the C-ABI library: it loads, exports every function include/kvss.h declares,
+and rejects bad arguments with the documented codes before any HIP call (so these run on a
+machine without a GPU; no compute call is made)."""
+
+import ctypes
+import os
+
+import pytest
+
+from kv_sparse_speculative_amd import kvss
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvss.LIB_PATH),
+                                reason="libkvss.so not built")
+
+FAKE = 0x1000     # a non-NULL address that is never dereferenced on the failure paths
+
+
+def _desc(**kw):
+    d = dict(k=FAKE, v=FAKE, block_table=FAKE, kv_lens=FAKE, batch=2, num_kv_heads=2,
+             head_dim=128, block_size=16, max_blocks=4, num_blocks=8, max_kv_len=64,
+             dtype=kvss.KVSS_BF16)
+    d.update(kw)
+    return kvss.kvss_kv(**d)
+
+
+def test_exports_every_declared_function():
+    names = kvss.declared_functions()
+    assert set(names) == set(kvss._SIGNATURES), names
+    lib = ctypes.CDLL(kvss.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert kvss.lib().kvss_version() == 1
+
+
+def _verify(d, Hq=8, T=5, ws=None, wsb=0, q=FAKE, out=FAKE, scale=0.1):
+    return kvss.lib().verify_attn_full(ctypes.byref(d), q, Hq, T, scale, out, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", 7, kvss.KVSS_EUNSUPPORTED),
+    ("head_dim", 96, kvss.KVSS_EUNSUPPORTED),
+    ("block_size", 8, kvss.KVSS_EUNSUPPORTED),
+    ("batch", -1, kvss.KVSS_EINVAL),
+    ("num_kv_heads", 0, kvss.KVSS_EINVAL),
+    ("max_kv_len", 65, kvss.KVSS_EINVAL),       # > max_blocks * block_size
+    ("k", None, kvss.KVSS_EINVAL),
+    ("block_table", None, kvss.KVSS_EINVAL),
+])
+def test_kv_descriptor_validation(field, value, code):
+    assert _verify(_desc(**{field: value})) == code
+    assert kvss.lib().kvss_last_error().decode()
+
+
+def test_verify_argument_validation():
+    d = _desc()
+    assert _verify(d, Hq=7) == kvss.KVSS_EINVAL              # not a multiple of Hkv
+    assert _verify(d, T=0) == kvss.KVSS_EINVAL
+    assert _verify(d, Hq=16, T=5) == kvss.KVSS_EUNSUPPORTED   # G * T = 40 > 32
+    assert _verify(d, q=None) == kvss.KVSS_EINVAL
+    assert _verify(d, scale=float("inf")) == kvss.KVSS_EINVAL
+    assert kvss.lib().verify_attn_full(None, FAKE, 8, 5, 0.1, FAKE, None, None, 0, None) == kvss.KVSS_EINVAL
+
+
+def test_workspace_too_small_is_rejected():
+    d = _desc(batch=64, num_kv_heads=8, max_blocks=2001, num_blocks=128064, max_kv_len=32005)
+    need = kvss.lib().kvss_verify_workspace_bytes(ctypes.byref(d), 32, 5)
+    assert need > 0                  # long contexts are split
+    assert _verify(d, Hq=32, T=5, ws=FAKE, wsb=need - 1) == kvss.KVSS_EWORKSPACE
+    assert _verify(d, Hq=32, T=5, ws=None, wsb=need) == kvss.KVSS_EWORKSPACE
+    assert "workspace" in kvss.lib().kvss_last_error().decode()
+
+
+def test_empty_batch_is_a_no_op():
+    d = _desc(batch=0, k=None, v=None, block_table=None, kv_lens=None)
+    assert _verify(d) == kvss.KVSS_OK
+    assert kvss.lib().kvss_last_error().decode() == ""
+
+
+def test_draft_and_snapkv_validation():
+    d = _desc()
+    L = kvss.lib()
+    assert L.draft_attn_sparse(ctypes.byref(d), FAKE, 8, None, None, 4, FAKE, 10, 0.1, FAKE, None,
+                               None, 0, None) == kvss.KVSS_EINVAL          # k_max > 0 needs a list
+    assert L.draft_attn_sparse(ctypes.byref(d), FAKE, 8, FAKE, FAKE, -1, FAKE, 10, 0.1, FAKE, None,
+                               None, 0, None) == kvss.KVSS_EINVAL
+    assert L.draft_attn_sparse(ctypes.byref(d), FAKE, 8, FAKE, FAKE, 4, FAKE, -2, 0.1, FAKE, None,
+                               None, 0, None) == kvss.KVSS_EINVAL
+    assert L.snapkv_select(ctypes.byref(d), FAKE, 8, 16, 7, 16, 0.1, FAKE, FAKE, None, None, 0,
+                           None) == kvss.KVSS_EINVAL                       # budget <= w
+    assert L.snapkv_select(ctypes.byref(d), FAKE, 8, 16, 6, 64, 0.1, FAKE, FAKE, None, None, 0,
+                           None) == kvss.KVSS_EINVAL                       # even pool
+    assert L.snapkv_select(ctypes.byref(d), FAKE, 8, 80, 7, 96, 0.1, FAKE, FAKE, None, None, 0,
+                           None) == kvss.KVSS_EUNSUPPORTED                 # G * w > 256
+    need = L.kvss_snapkv_workspace_bytes(ctypes.byref(d), 8, 16, 64)
+    assert need > 0
+    assert L.snapkv_select(ctypes.byref(d), FAKE, 8, 16, 7, 64, 0.1, FAKE, FAKE, None, FAKE,
+                           need - 1, None) == kvss.KVSS_EWORKSPACE
+
+
+def test_accept_and_streaming_validation():
+    L = kvss.lib()
+    args = [FAKE, FAKE, FAKE, 4, 3, 100, 1.0, 1, 0, FAKE, FAKE, None, None, 0, None]
+    assert L.spec_accept(*args) == kvss.KVSS_EWORKSPACE
+    bad = list(args); bad[6] = -1.0
+    assert L.spec_accept(*bad) == kvss.KVSS_EINVAL
+    bad = list(args); bad[5] = 1 << 24
+    assert L.spec_accept(*bad) == kvss.KVSS_EINVAL
+    bad = list(args); bad[1] = None
+    assert L.spec_accept(*bad) == kvss.KVSS_EINVAL                         # temperature > 0 needs q
+    assert L.kvss_accept_workspace_bytes(4, 3, 100) >= 4 * 7 * 16
+    assert L.kvss_streaming_set(FAKE, 2, 2, -1, 4, FAKE, FAKE, FAKE, None) == kvss.KVSS_EINVAL
+    assert L.kvss_streaming_set(None, 2, 2, 4, 4, FAKE, FAKE, FAKE, None) == kvss.KVSS_EINVAL
