@@ -7,16 +7,21 @@
 // (sequence, KV head)'s K and V exactly once per launch and keeps all G * T query rows of
 // that KV head (GQA, Section 3.2) on the same bytes.
 //
-// Work decomposition: grid (split, KV head, sequence); 4 waves per workgroup; each wave takes
-// 32-key chunks of the split round-robin. Per chunk and wave:
-//   S^T (16 keys x 16 rows tiles) = K . Q^T   with v_mfma_f32_16x16x32_bf16: K rows come
-//       straight from HBM as the A operand (16 B per lane, one key row per 16 lanes), Q^T is
-//       resident in registers as the B operand;
-//   online softmax in the log2 domain (row max/sum across the 4 lane groups with xor
-//       shuffles; each lane owns one query row of the C tile);
-//   O^T (16 dims x 16 rows) += V^T . P^T  with P split into bf16 hi + lo parts (two MFMAs) so
-//       that P carries ~16 mantissa bits; V^T is read transposed from a padded LDS tile
-//       that the same wave wrote.
+// Work decomposition: grid (split, KV head, sequence); 4 waves per workgroup (one per SIMD);
+// each wave takes 32-key chunks of the split round-robin.
+//   Prologue: the workgroup translates the split's keys into physical cache rows once (block
+//     table, and for a draft the selection list) into an LDS table, so no dependent global
+//     read sits in front of a K/V load in the main loop.
+//   Main loop, register double-buffered: the K and V rows of the wave's next chunk are in
+//     flight while the current chunk is computed:
+//     S^T (16 keys x 16 rows tiles) = K . Q^T with v_mfma_f32_16x16x32_bf16; K rows come from
+//       HBM as the A operand (16 B per lane, one key row per 16 lanes); Q^T stays resident in
+//       registers as the B operand;
+//     online softmax in the log2 domain (row max across the 4 lane groups with xor shuffles;
+//       each lane owns one query row of the C tile);
+//     O^T (16 dims x 16 rows) += V^T . P^T with P split into bf16 hi + lo parts (two MFMAs) so
+//       that P carries ~16 mantissa bits; V^T is read transposed from a padded LDS tile that
+//       the same wave wrote.
 // Waves merge (max, sum, O) through LDS; with one split the workgroup writes the final
 // normalised output, otherwise (m, l, o) partials that the merge kernel combines.
 
@@ -27,6 +32,7 @@ namespace kvss {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr unsigned kInvalidRow = 0xffffffffu;
 
 template <int D>
 struct MfmaCfg {
@@ -34,8 +40,9 @@ struct MfmaCfg {
     static constexpr int DT = D / 16;          // dim tiles of the PV product
     static constexpr int STRIDE = D + 4;       // LDS row stride in bf16 (row = D/2 + 2 dwords)
     static constexpr int VLDS = kWaves * 32 * STRIDE * 2;            // bytes
+    static constexpr int TAB = (kMfmaTableEntries + 1) * 4;          // bytes
     static constexpr int MERGE = kWaves * 32 * (D + 2) * 4;          // bytes
-    static constexpr int SMEM = VLDS > MERGE ? VLDS : MERGE;
+    static constexpr int SMEM = (VLDS + TAB) > MERGE ? (VLDS + TAB) : MERGE;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
@@ -44,17 +51,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
     return r;
 }
 
-template <int D, bool GATHER>
+template <int D, bool GATHER, int NRT>
 __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
     using C = MfmaCfg<D>;
     constexpr int KS = C::KS, DT = C::DT, STRIDE = C::STRIDE;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
     __shared__ int s_bad;
 
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
     const int m16 = lane & 15, q4 = lane >> 4;
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    if (threadIdx.x == 0) s_bad = 0;
+    if (tid == 0) s_bad = 0;
 
     const int L = max(min(a.kv_lens[b], a.max_kv_len), 0);
     int n_list = 0, lo = 0;
@@ -66,16 +74,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
     const int v_begin = split * a.split_len;
     const int v_end = (split == a.nsplit - 1) ? total : min(v_begin + a.split_len, total);
 
-    const PagedCache cache{a.block_table, a.Hkv, a.bs, a.max_blocks, a.num_blocks, D};
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     const uint16_t* vp = static_cast<const uint16_t*>(a.v);
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+    const int bs = a.bs;
 
     // Q^T as the B operand: lane supplies column (row) rt*16 + m16, dims ks*32 + q4*8 .. +7.
-    bf16x8 qop[2][KS];
-    int limit[2];
+    bf16x8 qop[NRT][KS];
+    int limit[NRT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < NRT; ++rt) {
         const int r = rt * 16 + m16;
         limit[rt] = -1;
         if (r < a.R) {
@@ -91,152 +99,211 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
         }
     }
 
-    f32x4 o[DT][2];
+    f32x4 o[DT][NRT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt][0] = o[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mrow[2] = {kNegInf, kNegInf};
-    float lrow[2] = {0.f, 0.f};
-    bool bad = false;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrow[NRT], lrow[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) { mrow[rt] = kNegInf; lrow[rt] = 0.f; }
 
     uint16_t* vl = reinterpret_cast<uint16_t*>(smem) + wid * 32 * STRIDE;
+    unsigned* rowtab = reinterpret_cast<unsigned*>(smem + C::VLDS);
     const int32_t* sel = GATHER ? a.sel_idx + ((size_t)b * a.Hkv + g) * a.k_max : nullptr;
+    const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
 
-    for (int c0 = v_begin + wid * 32; c0 < v_end; c0 += kWaves * 32) {
-        uint4 kr[2][KS], vr[2][KS];
-        unsigned okmask[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const int v = c0 + kt * 16 + m16;
-            bool ok = v < v_end;
-            int pos = v;
-            if constexpr (GATHER) {
+    // Segment = the keys whose rows one LDS table holds (the planner keeps a split to one).
+    const int seg_keys = GATHER ? kMfmaTableEntries : kMfmaTableEntries * bs;
+    for (int seg = v_begin; seg < v_end; seg += seg_keys) {
+        const int seg_end = min(seg + seg_keys, v_end);
+        const int blk0 = seg / bs;
+        __syncthreads();                          // previous segment's table is no longer read
+        if constexpr (GATHER) {
+            for (int i = tid; i < seg_end - seg; i += kWaves * 64) {
+                const int v = seg + i;
+                int pos = v;
+                bool ok = true;
+                if (v < n_list) { pos = sel[v]; ok = pos >= 0 && pos < lo; }
+                else pos = lo + (v - n_list);
+                unsigned row = kInvalidRow;
                 if (ok) {
-                    if (v < n_list) {
-                        pos = sel[v];
-                        ok = (pos >= 0) && (pos < lo);
-                    } else {
-                        pos = lo + (v - n_list);
-                    }
+                    const int blk = btab[pos / bs];
+                    if ((unsigned)blk < (unsigned)a.num_blocks)
+                        row = ((unsigned)blk * a.Hkv + g) * bs + pos % bs;
+                    else
+                        s_bad = 1;
                 }
+                rowtab[i] = row;
             }
-            size_t off = 0;
-            if (ok) {
-                if (!cache.row_offset(b, g, pos, off)) { bad = true; ok = false; }
-            }
-            okmask[kt] = (unsigned)(__ballot(ok) & 0xffffull);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (ok) {
-                    kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32 + q4 * 8);
-                    vr[kt][ks] = *reinterpret_cast<const uint4*>(vp + off + ks * 32 + q4 * 8);
-                } else {
-                    kr[kt][ks] = make_uint4(0, 0, 0, 0);
-                    vr[kt][ks] = make_uint4(0, 0, 0, 0);
-                }
+        } else {
+            const int nblk = (seg_end - 1) / bs - blk0 + 1;
+            for (int i = tid; i < nblk; i += kWaves * 64) {
+                const int blk = btab[blk0 + i];
+                unsigned row = kInvalidRow;
+                if ((unsigned)blk < (unsigned)a.num_blocks) row = ((unsigned)blk * a.Hkv + g) * bs;
+                else s_bad = 1;
+                rowtab[i] = row;
             }
         }
+        __syncthreads();
 
-        // V rows -> this wave's LDS tile (row = key within chunk).
-        wave_lds_order();
+        // Issue the K/V loads of one 32-key chunk into registers.
+        auto issue = [&](int c0, uint4 (&kr)[2][KS], uint4 (&vr)[2][KS], unsigned (&okm)[2]) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < 2; ++kt) {
+                const int v = c0 + kt * 16 + m16;
+                unsigned row = kInvalidRow;
+                if (v < seg_end) {
+                    if constexpr (GATHER) {
+                        row = rowtab[v - seg];
+                    } else {
+                        const unsigned base = rowtab[v / bs - blk0];
+                        row = base == kInvalidRow ? kInvalidRow : base + (unsigned)(v % bs);
+                    }
+                }
+                const bool ok = row != kInvalidRow;
+                okm[kt] = (unsigned)(__ballot(ok) & 0xffffull);
+                // Masked keys load cache row 0 (always a valid address) and are discarded:
+                // their scores become -inf and their V rows are zeroed when consumed.
+                const size_t off = (size_t)(ok ? row : 0u) * D + q4 * 8;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                *reinterpret_cast<uint4*>(vl + (kt * 16 + m16) * STRIDE + ks * 32 + q4 * 8) = vr[kt][ks];
+                for (int ks = 0; ks < KS; ++ks) {
+                    kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32);
+                    vr[kt][ks] = *reinterpret_cast<const uint4*>(vp + off + ks * 32);
+                }
+            }
+        };
 
-        // S^T = K . Q^T : C tile [key 4*q4+i][row m16].
-        f32x4 sacc[2][2];
+        // Fold one chunk into the running softmax state.
+        auto consume = [&](int c0, uint4 (&kr)[2][KS], uint4 (&vr)[2][KS], unsigned (&okm)[2]) {
+            wave_lds_order();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < 2; ++kt) {
+                const bool ok = (okm[kt] >> m16) & 1u;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[kt][ks]), qop[rt][ks],
-                                                                 acc, 0, 0, 0);
-                sacc[kt][rt] = acc;
+                    *reinterpret_cast<uint4*>(vl + (kt * 16 + m16) * STRIDE + ks * 32 + q4 * 8) =
+                        ok ? vr[kt][ks] : make_uint4(0, 0, 0, 0);
             }
 
-        bf16x8 phi[2], plo[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            float sv[8];
-            float cmax = kNegInf;
+            // S^T = K . Q^T : C tile [key 4*q4+i][row m16].
+            f32x4 sacc[2][NRT];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kt * 16 + q4 * 4 + i;
-                    bool allowed = (okmask[kt] >> (q4 * 4 + i)) & 1u;
-                    if constexpr (!GATHER) allowed = allowed && (c0 + key <= limit[rt]);
-                    const float x = allowed ? sacc[kt][rt][i] * a.scale_log2 : kNegInf;
-                    sv[kt * 4 + i] = x;
-                    cmax = fmaxf(cmax, x);
+                for (int rt = 0; rt < NRT; ++rt) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[kt][ks]),
+                                                                     qop[rt][ks], acc, 0, 0, 0);
+                    sacc[kt][rt] = acc;
                 }
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-            const float mnew = fmaxf(mrow[rt], cmax);
-            const float muse = (mnew == kNegInf) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrow[rt] - muse);
-            mrow[rt] = mnew;
-            float psum = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = __builtin_amdgcn_exp2f(sv[j] - muse);
-                const __bf16 hi = (__bf16)p;
-                phi[rt][j] = hi;
-                plo[rt][j] = (__bf16)(p - (float)hi);
-                psum += p;
-            }
-            lrow[rt] = lrow[rt] * alpha + psum;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
-        }
 
-        // O^T += V^T . P^T. k-slot j of lane group q4 is key 16*(j/4) + 4*q4 + (j%4), matching
-        // the C-tile keys this lane holds in sacc[j/4][*][j%4].
-        wave_lds_order();
+            bf16x8 phi[NRT], plo[NRT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            uint32_t w[4];
+            for (int rt = 0; rt < NRT; ++rt) {
+                float sv[8];
+                float cmax = kNegInf;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int k0 = 16 * (p >> 1) + 4 * q4 + 2 * (p & 1);    // slot j = 2p
-                w[p] = (uint32_t)vl[k0 * STRIDE + dt * 16 + m16] |
-                       ((uint32_t)vl[(k0 + 1) * STRIDE + dt * 16 + m16] << 16);
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = kt * 16 + q4 * 4 + i;
+                        bool allowed = (okm[kt] >> (q4 * 4 + i)) & 1u;
+                        if constexpr (!GATHER) allowed = allowed && (c0 + key <= limit[rt]);
+                        const float x = allowed ? sacc[kt][rt][i] * a.scale_log2 : kNegInf;
+                        sv[kt * 4 + i] = x;
+                        cmax = fmaxf(cmax, x);
+                    }
+                cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+                cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+                const float mnew = fmaxf(mrow[rt], cmax);
+                const float muse = (mnew == kNegInf) ? 0.f : mnew;
+                const float alpha = __builtin_amdgcn_exp2f(mrow[rt] - muse);
+                mrow[rt] = mnew;
+                float psum = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float p = __builtin_amdgcn_exp2f(sv[j] - muse);
+                    const __bf16 hi = (__bf16)p;
+                    phi[rt][j] = hi;
+                    plo[rt][j] = (__bf16)(p - (float)hi);
+                    psum += p;
+                }
+                lrow[rt] = lrow[rt] * alpha + psum;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
             }
-            const bf16x8 av = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+
+            // O^T += V^T . P^T. k-slot j of lane group q4 is key 16*(j/4) + 4*q4 + (j%4),
+            // matching the C-tile keys this lane holds in sacc[j/4][*][j%4]. The V^T operand
+            // comes from the transposing LDS read: in each 16-lane group, lane i receives
+            // element i%4 of the 8-byte rows addressed by lanes 4k + i/4 (k = 0..3). Lane s
+            // addresses V[key 4*q4 + s/4 (+16)][dt*16 + 4*(s%4)], so lane m receives
+            // V[4*q4 + k (+16)][dt*16 + m] for k = 0..3: slots j = 0..3 (and 4..7).
+            wave_lds_order();
+            const int trow = 4 * q4 + (m16 >> 2), tcol = 4 * (m16 & 3);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi[rt], o[dt][rt], 0, 0, 0);
-                o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo[rt], o[dt][rt], 0, 0, 0);
+            for (int dt = 0; dt < DT; ++dt) {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(vl + trow * STRIDE + dt * 16 + tcol));
+                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(vl + (trow + 16) * STRIDE + dt * 16 + tcol));
+                uint4 wv;
+                __builtin_memcpy(&wv.x, &lo4, 8);
+                __builtin_memcpy(&wv.z, &hi4, 8);
+                const bf16x8 av = as_bf16x8(wv);
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt) {
+                    o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi[rt], o[dt][rt], 0, 0, 0);
+                    o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo[rt], o[dt][rt], 0, 0, 0);
+                }
             }
+            wave_lds_order();
+        };
+
+        // Double-buffered walk over this wave's chunks: chunk c+stride loads while c computes.
+        // Issues are unconditional (a chunk past the end loads a dummy row and is fully
+        // masked) so that every path reaches a consume with the same loads outstanding and
+        // the compiler's wait before it only covers the chunk being consumed.
+        constexpr int stride = kWaves * 32;
+        uint4 kA[2][KS], vA[2][KS], kB[2][KS], vB[2][KS];
+        unsigned okA[2], okB[2];
+        int c = seg + wid * 32;
+        issue(c, kA, vA, okA);
+        for (; c < seg_end; c += 2 * stride) {
+            issue(c + stride, kB, vB, okB);
+            consume(c, kA, vA, okA);
+            if (c + stride >= seg_end) break;
+            issue(c + 2 * stride, kA, vA, okA);
+            consume(c + stride, kB, vB, okB);
         }
-        wave_lds_order();
     }
 
     // Row sums were kept per lane group; complete them.
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < NRT; ++rt) {
         lrow[rt] += __shfl_xor(lrow[rt], 16);
         lrow[rt] += __shfl_xor(lrow[rt], 32);
     }
 
     __syncthreads();                 // every wave is done with its V tile (smem is reused)
-    if (__ballot(bad) != 0ull && lane == 0) s_bad = 1;
     float* so = reinterpret_cast<float*>(smem);               // [wave][32 rows][D]
     float* sml = so + kWaves * 32 * D;                         // [wave][32 rows][2]
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 so[(wid * 32 + rt * 16 + m16) * D + dt * 16 + q4 * 4 + i] = o[dt][rt][i];
     if (q4 == 0) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < NRT; ++rt) {
             sml[(wid * 32 + rt * 16 + m16) * 2 + 0] = mrow[rt];
             sml[(wid * 32 + rt * 16 + m16) * 2 + 1] = lrow[rt];
         }
@@ -245,7 +312,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
 
     const bool poisoned = s_bad != 0;
     const float qnan = __builtin_nanf("");
-    for (int idx = threadIdx.x; idx < a.R * D; idx += kWaves * 64) {
+    for (int idx = tid; idx < a.R * D; idx += kWaves * 64) {
         const int r = idx / D, d = idx % D;
         float M = kNegInf;
 #pragma unroll
@@ -280,16 +347,23 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
     }
 }
 
+template <int D, int NRT>
+void launch_d(const AttnArgs& a, bool gather, dim3 grid, dim3 block, hipStream_t s) {
+    if (gather) attn_mfma_kernel<D, true, NRT><<<grid, block, 0, s>>>(a);
+    else attn_mfma_kernel<D, false, NRT><<<grid, block, 0, s>>>(a);
+}
+
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool gather, hipStream_t s) {
     dim3 grid(a.nsplit, a.Hkv, a.B), block(kWaves * 64);
+    const bool one = a.R <= 16;
     if (a.D == 128) {
-        if (gather) attn_mfma_kernel<128, true><<<grid, block, 0, s>>>(a);
-        else attn_mfma_kernel<128, false><<<grid, block, 0, s>>>(a);
+        if (one) launch_d<128, 1>(a, gather, grid, block, s);
+        else launch_d<128, 2>(a, gather, grid, block, s);
     } else {
-        if (gather) attn_mfma_kernel<64, true><<<grid, block, 0, s>>>(a);
-        else attn_mfma_kernel<64, false><<<grid, block, 0, s>>>(a);
+        if (one) launch_d<64, 1>(a, gather, grid, block, s);
+        else launch_d<64, 2>(a, gather, grid, block, s);
     }
     return hipGetLastError();
 }

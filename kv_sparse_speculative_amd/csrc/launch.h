@@ -6,6 +6,10 @@
 
 namespace kvss {
 
+// Physical-row entries one bf16 attention workgroup keeps in LDS: per key for a gathered set,
+// per cache block for a dense range.
+constexpr int kMfmaTableEntries = 4096;
+
 // One attention launch: R = G * T query rows per (sequence, KV head) over a key set that is
 // either the dense causal range [0, L) (verify) or a gathered list + dense tail (draft).
 struct AttnArgs {
