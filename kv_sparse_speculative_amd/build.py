@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvss.so")
-SOURCES = ["api.hip", "attn_mfma.hip", "attn_simple.hip", "merge.hip", "snapkv.hip",
+SOURCES = ["api.hip", "attn_mfma.hip", "attn_simple.hip", "merge.hip", "snapkv.hip", "snapkv_mfma.hip",
            "accept.hip", "streaming.hip"]
 
 HIPCC_FLAGS = [

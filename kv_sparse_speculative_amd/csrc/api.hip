@@ -51,14 +51,16 @@ struct Plan {
 
 // Split a virtual key range of up to max_total keys per (sequence, KV head) so that the
 // launch offers about kTargetWorkgroups workgroups, each doing at least four rounds.
-Plan plan_splits(long pairs, long max_total, int unit) {
+Plan plan_splits(long pairs, long max_total, int unit, long max_len = 1L << 30) {
     Plan p{1, unit};
     if (max_total <= 0 || pairs <= 0) return p;
     const long want = ceil_div(kTargetWorkgroups, pairs);
     const long useful = ceil_div(max_total, 4L * unit);
     long ns = want < useful ? want : useful;
     if (ns < 1) ns = 1;
-    const long len = ceil_div(ceil_div(max_total, ns), unit) * unit;
+    if (ceil_div(max_total, ns) > max_len) ns = ceil_div(max_total, max_len);
+    long len = ceil_div(ceil_div(max_total, ns), unit) * unit;
+    if (len > max_len) len = max_len / unit * unit;
     p.split_len = (int)len;
     p.nsplit = (int)ceil_div(max_total, len);
     return p;
@@ -145,7 +147,11 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     SnapLayout s{};
     const int G = num_q_heads / kv->num_kv_heads;
     s.R = G * w;
-    s.p1 = plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kSimpleUnit);
+    // bf16 splits must fit one LDS table of block bases (kMfmaTableEntries - 1 blocks).
+    s.p1 = kv->dtype == KVSS_BF16
+               ? plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kMfmaUnit,
+                             (long)(kvss::kMfmaTableEntries - 1) * kv->block_size)
+               : plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kSimpleUnit);
     s.n_stride = kv->max_kv_len > w ? kv->max_kv_len - w : 0;
     const size_t rows = (size_t)kv->batch * kv->num_kv_heads;
     s.part1 = align_up(rows * s.R * s.p1.nsplit * 2 * sizeof(float));

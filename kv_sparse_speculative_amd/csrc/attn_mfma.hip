@@ -34,16 +34,21 @@ namespace {
 constexpr int kWaves = 4;
 constexpr unsigned kInvalidRow = 0xffffffffu;
 
-template <int D>
+template <int D, int NRT>
 struct MfmaCfg {
     static constexpr int KS = D / 32;          // k-steps of the QK^T contraction
     static constexpr int DT = D / 16;          // dim tiles of the PV product
+    static constexpr int ROWS = 16 * NRT;      // query rows held per wave
     static constexpr int STRIDE = D + 4;       // LDS row stride in bf16 (row = D/2 + 2 dwords)
     static constexpr int VLDS = kWaves * 32 * STRIDE * 2;            // bytes
     static constexpr int TAB = (kMfmaTableEntries + 1) * 4;          // bytes
-    static constexpr int MERGE = kWaves * 32 * (D + 2) * 4;          // bytes
+    static constexpr int MERGE = kWaves * ROWS * (D + 2) * 4;        // bytes
     static constexpr int SMEM = (VLDS + TAB) > MERGE ? (VLDS + TAB) : MERGE;
 };
+
+// Entries of the physical-row table one thread fills per pass of the prologue; their global
+// reads are all issued before any is waited on.
+constexpr int kTabUnroll = 4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
     bf16x8 r;
@@ -51,10 +56,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
     return r;
 }
 
+// With one row tile the kernel fits two workgroups per CU (<= 256 registers per lane), so a
+// draft launch of B * Hkv workgroups is resident in a single round.
 template <int D, bool GATHER, int NRT>
-__global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
-    using C = MfmaCfg<D>;
-    constexpr int KS = C::KS, DT = C::DT, STRIDE = C::STRIDE;
+__global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
+    using C = MfmaCfg<D, NRT>;
+    constexpr int KS = C::KS, DT = C::DT, STRIDE = C::STRIDE, ROWS = C::ROWS;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
     __shared__ int s_bad;
 
@@ -120,30 +127,58 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
         const int blk0 = seg / bs;
         __syncthreads();                          // previous segment's table is no longer read
         if constexpr (GATHER) {
-            for (int i = tid; i < seg_end - seg; i += kWaves * 64) {
-                const int v = seg + i;
-                int pos = v;
-                bool ok = true;
-                if (v < n_list) { pos = sel[v]; ok = pos >= 0 && pos < lo; }
-                else pos = lo + (v - n_list);
-                unsigned row = kInvalidRow;
-                if (ok) {
-                    const int blk = btab[pos / bs];
-                    if ((unsigned)blk < (unsigned)a.num_blocks)
-                        row = ((unsigned)blk * a.Hkv + g) * bs + pos % bs;
-                    else
-                        s_bad = 1;
+            const int n = seg_end - seg;
+            for (int base = 0; base < n; base += kTabUnroll * kWaves * 64) {
+                int pos[kTabUnroll];
+                bool ok[kTabUnroll];
+#pragma unroll
+                for (int u = 0; u < kTabUnroll; ++u) {       // selection-list reads
+                    const int v = seg + base + u * kWaves * 64 + tid;
+                    ok[u] = v < seg_end;
+                    pos[u] = lo + (v - n_list);
+                    if (ok[u] && v < n_list) {
+                        pos[u] = sel[v];
+                        ok[u] = pos[u] >= 0 && pos[u] < lo;
+                    }
                 }
-                rowtab[i] = row;
+                int blk[kTabUnroll];
+#pragma unroll
+                for (int u = 0; u < kTabUnroll; ++u)         // block-table reads
+                    blk[u] = ok[u] ? btab[pos[u] / bs] : 0;
+#pragma unroll
+                for (int u = 0; u < kTabUnroll; ++u) {
+                    const int i = base + u * kWaves * 64 + tid;
+                    if (i >= n) continue;
+                    unsigned row = kInvalidRow;
+                    if (ok[u]) {
+                        if ((unsigned)blk[u] < (unsigned)a.num_blocks)
+                            row = ((unsigned)blk[u] * a.Hkv + g) * bs + pos[u] % bs;
+                        else
+                            s_bad = 1;
+                    }
+                    rowtab[i] = row;
+                }
             }
         } else {
             const int nblk = (seg_end - 1) / bs - blk0 + 1;
-            for (int i = tid; i < nblk; i += kWaves * 64) {
-                const int blk = btab[blk0 + i];
-                unsigned row = kInvalidRow;
-                if ((unsigned)blk < (unsigned)a.num_blocks) row = ((unsigned)blk * a.Hkv + g) * bs;
-                else s_bad = 1;
-                rowtab[i] = row;
+            for (int base = 0; base < nblk; base += kTabUnroll * kWaves * 64) {
+                int blk[kTabUnroll];
+#pragma unroll
+                for (int u = 0; u < kTabUnroll; ++u) {
+                    const int i = base + u * kWaves * 64 + tid;
+                    blk[u] = i < nblk ? btab[blk0 + i] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < kTabUnroll; ++u) {
+                    const int i = base + u * kWaves * 64 + tid;
+                    if (i >= nblk) continue;
+                    unsigned row = kInvalidRow;
+                    if ((unsigned)blk[u] < (unsigned)a.num_blocks)
+                        row = ((unsigned)blk[u] * a.Hkv + g) * bs;
+                    else
+                        s_bad = 1;
+                    rowtab[i] = row;
+                }
             }
         }
         __syncthreads();
@@ -292,20 +327,20 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
     }
 
     __syncthreads();                 // every wave is done with its V tile (smem is reused)
-    float* so = reinterpret_cast<float*>(smem);               // [wave][32 rows][D]
-    float* sml = so + kWaves * 32 * D;                         // [wave][32 rows][2]
+    float* so = reinterpret_cast<float*>(smem);               // [wave][ROWS][D]
+    float* sml = so + kWaves * ROWS * D;                       // [wave][ROWS][2]
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                so[(wid * 32 + rt * 16 + m16) * D + dt * 16 + q4 * 4 + i] = o[dt][rt][i];
+                so[(wid * ROWS + rt * 16 + m16) * D + dt * 16 + q4 * 4 + i] = o[dt][rt][i];
     if (q4 == 0) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            sml[(wid * 32 + rt * 16 + m16) * 2 + 0] = mrow[rt];
-            sml[(wid * 32 + rt * 16 + m16) * 2 + 1] = lrow[rt];
+            sml[(wid * ROWS + rt * 16 + m16) * 2 + 0] = mrow[rt];
+            sml[(wid * ROWS + rt * 16 + m16) * 2 + 1] = lrow[rt];
         }
     }
     __syncthreads();
@@ -316,14 +351,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_mfma_kernel(AttnArgs a) {
         const int r = idx / D, d = idx % D;
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sml[(w * 32 + r) * 2]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sml[(w * ROWS + r) * 2]);
         float lsum = 0.f, osum = 0.f;
         if (M != kNegInf) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                const float e = __builtin_amdgcn_exp2f(sml[(w * 32 + r) * 2] - M);
-                lsum += e * sml[(w * 32 + r) * 2 + 1];
-                osum += e * so[(w * 32 + r) * D + d];
+                const float e = __builtin_amdgcn_exp2f(sml[(w * ROWS + r) * 2] - M);
+                lsum += e * sml[(w * ROWS + r) * 2 + 1];
+                osum += e * so[(w * ROWS + r) * D + d];
             }
         }
         const int h = g * a.G + r / a.T, t = r % a.T;

@@ -10,6 +10,9 @@ namespace kvss {
 // per cache block for a dense range.
 constexpr int kMfmaTableEntries = 4096;
 
+// Candidate keys one workgroup of the bf16 SnapKV column-score pass covers.
+constexpr int kSnapColKeys = 2048;
+
 // One attention launch: R = G * T query rows per (sequence, KV head) over a key set that is
 // either the dense causal range [0, L) (verify) or a gathered list + dense tail (draft).
 struct AttnArgs {
@@ -55,6 +58,7 @@ struct SnapArgs {
 };
 
 hipError_t launch_snapkv(const SnapArgs& a, hipStream_t s);
+hipError_t launch_snapkv_mfma_passes(const SnapArgs& a, hipStream_t s);
 
 hipError_t launch_streaming_set(const int32_t* kv_lens, int B, int Hkv, int sink, int window,
                                 int32_t* sel_idx, int32_t* sel_count, int32_t* tail_lo,

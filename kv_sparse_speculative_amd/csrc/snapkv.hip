@@ -262,7 +262,11 @@ hipError_t launch_typed(const SnapArgs& a, hipStream_t s) {
 
 hipError_t launch_snapkv(const SnapArgs& a, hipStream_t s) {
     if (a.dtype == 1) {
-        return a.D == 128 ? launch_typed<uint16_t, 128>(a, s) : launch_typed<uint16_t, 64>(a, s);
+        // bf16: matrix-core score passes, then pool + top-k.
+        hipError_t e = launch_snapkv_mfma_passes(a, s);
+        if (e != hipSuccess) return e;
+        snap_topk_kernel<<<dim3(a.Hkv, a.B), 1024, 0, s>>>(a);
+        return hipGetLastError();
     }
     return a.D == 128 ? launch_typed<float, 128>(a, s) : launch_typed<float, 64>(a, s);
 }
