@@ -184,6 +184,7 @@ KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads
  *     offset low 32 bits); stream 0 word 0 gives u_i, stream 1 word x % 4 of block x / 4
  *     gives u'_x; a 32-bit word x maps to (x >> 9) * 2^-23 + 2^-24. Callers advance `offset`
  *     between calls that share a seed.
+ *   Limits: 0 <= gamma <= 31 (KVSS_EUNSUPPORTED above), 1 <= vocab < 2^24.
  *   out_tokens       int32 [batch, gamma + 1]: emitted tokens, then -1.
  *   out_num_accepted int32 [batch]: accepted draft tokens, 0 .. gamma.
  *   row_stats        float32 [batch, 2 * gamma + 1, 4] or NULL: per logit row (target rows

@@ -1,15 +1,17 @@
 // Speculative acceptance (MagicDec Section 3.1: the speculative-decoding rule of Leviathan et
 // al., whose expected yield is Eq. (1); Section 5.1: greedy decoding in the experiments).
 //
-// Two kernels:
-//   stats  : one workgroup per logit row (target rows 0..gamma, draft rows 0..gamma-1) streams
-//            the vocabulary once with 16-byte loads and reduces max(z/temp), sum exp(z/temp -
-//            max), the argmax (lowest id on ties) and z/temp at the row's draft token;
-//   decide : one workgroup per sequence. Lane 0 walks the gamma accept tests (greedy argmax
-//            match, or u_i < p_i(x_i) / q_i(x_i) with Philox uniforms); the whole workgroup
-//            then runs the exponential race argmin_x -log(u'_x) / w(x) over the emitting row
-//            (w = max(0, p - q) after a rejection, p after full acceptance), re-reading only
-//            that row pair.
+// Kernels, in launch order:
+//   stats    grid (slice, row, sequence): each workgroup streams one slice of one logit row
+//            (target rows 0..gamma, draft rows 0..gamma-1) once with 16-byte loads and writes a
+//            partial (max of z/temp, sum of exp(z/temp - max), max z, its lowest index);
+//   decide   one wave per sequence: merges the partials into row statistics, walks the gamma
+//            accept tests (greedy argmax match, or u_i < p_i(x_i) / q_i(x_i) with Philox
+//            uniforms) and writes the accepted prefix, the count and the emitting position;
+//   race     (sampling only) grid (slice, sequence): exponential race argmin_x -log(u'_x) / w(x)
+//            over one slice of the emitting row, w = max(0, p - q) after a rejection (p if that
+//            is all zero) or p after full acceptance; re-reads only that row pair;
+//   finalize (sampling only) one wave per sequence: the winning token of the slices.
 
 #include "common.h"
 #include "launch.h"
@@ -18,152 +20,209 @@ namespace kvss {
 namespace {
 
 constexpr int kStatThreads = 256;
-constexpr int kRaceThreads = 1024;
+constexpr int kRaceThreads = 256;
 
-struct MaxSum {
-    float m, s;
+struct Part {          // per (sequence, row, slice)
+    float m, s, zmax;
+    int imax;
 };
-
-__device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b) {
-    const float M = fmaxf(a.m, b.m);
-    if (M == kNegInf) return {kNegInf, 0.f};
-    return {M, a.s * __expf(a.m - M) + b.s * __expf(b.m - M)};
-}
-
-// argmax with lowest-index tie-break
-__device__ __forceinline__ void am_merge(float& v, int& i, float v2, int i2) {
-    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
-}
-
-template <bool GREEDY>
-__global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a) {
-    __shared__ float sm[kStatThreads / 64], ss[kStatThreads / 64], sv[kStatThreads / 64];
-    __shared__ int si[kStatThreads / 64];
-    const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int gamma = a.gamma, V = a.V;
-    const float* z = (r <= gamma) ? a.target + ((size_t)b * (gamma + 1) + r) * V
-                                  : a.draft + ((size_t)b * gamma + (r - gamma - 1)) * V;
-    const float it = a.inv_temp;
-    float m = kNegInf, s = 0.f, best = kNegInf;
-    int bi = 0x7fffffff;
-
-    auto visit = [&](float zv, int x) {
-        if (zv > best) { best = zv; bi = x; }      // visiting in increasing x per thread
-        if constexpr (!GREEDY) {
-            const float y = zv * it;
-            if (y > m) { s = s * __expf(m - y) + 1.f; m = y; }
-            else s += __expf(y - m);
-        }
-    };
-    if ((V & 3) == 0) {
-        const float4* z4 = reinterpret_cast<const float4*>(z);
-        for (int j = tid; j < V / 4; j += kStatThreads) {
-            const float4 v = z4[j];
-            visit(v.x, 4 * j); visit(v.y, 4 * j + 1); visit(v.z, 4 * j + 2); visit(v.w, 4 * j + 3);
-        }
-    } else {
-        for (int j = tid; j < V; j += kStatThreads) visit(z[j], j);
-    }
-    // wave reduce
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-        const float b2 = __shfl_xor(best, o);
-        const int i2 = __shfl_xor(bi, o);
-        if constexpr (!GREEDY) { const MaxSum t = ms_merge({m, s}, {m2, s2}); m = t.m; s = t.s; }
-        am_merge(best, bi, b2, i2);
-    }
-    const int lane = tid & 63, wid = tid >> 6;
-    if (lane == 0) { sm[wid] = m; ss[wid] = s; sv[wid] = best; si[wid] = bi; }
-    __syncthreads();
-    if (tid == 0) {
-        for (int w = 1; w < kStatThreads / 64; ++w) {
-            if constexpr (!GREEDY) { const MaxSum t = ms_merge({m, s}, {sm[w], ss[w]}); m = t.m; s = t.s; }
-            am_merge(best, bi, sv[w], si[w]);
-        }
-        float zx = 0.f;
-        if (!GREEDY && r != gamma) {
-            const int i = (r < gamma) ? r : r - gamma - 1;
-            const int x = a.tokens[(size_t)b * gamma + i];
-            zx = (x >= 0 && x < V) ? z[x] * it : kNegInf;
-        }
-        float* st = a.stats + ((size_t)b * (2 * gamma + 1) + r) * 4;
-        st[0] = GREEDY ? 0.f : m;
-        st[1] = GREEDY ? 0.f : s;
-        st[2] = zx;
-        st[3] = (float)bi;
-    }
-}
 
 struct RaceKey {
     float key;
     int x;
 };
 
+struct Decision {      // per sequence
+    int pos;           // emitting position (= number accepted)
+    int pad[3];
+};
+
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+    const float M = fmaxf(m, m2);
+    if (M == kNegInf) { m = kNegInf; s = 0.f; return; }
+    s = s * __expf(m - M) + s2 * __expf(m2 - M);
+    m = M;
+}
+
+__device__ __forceinline__ void am_merge(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
 __device__ __forceinline__ void race_merge(RaceKey& a, RaceKey b) {
     if (b.key < a.key || (b.key == a.key && b.x < a.x)) a = b;
 }
 
-__global__ __launch_bounds__(kRaceThreads) void accept_decide_kernel(AcceptArgs a) {
-    __shared__ int s_pos;
-    __shared__ RaceKey sr[kRaceThreads / 64], sp[kRaceThreads / 64];
-    const int b = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ const float* row_ptr(const AcceptArgs& a, int b, int r) {
+    const int gamma = a.gamma;
+    return (r <= gamma) ? a.target + ((size_t)b * (gamma + 1) + r) * a.V
+                        : a.draft + ((size_t)b * gamma + (r - gamma - 1)) * a.V;
+}
+
+template <bool GREEDY>
+__global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a, Part* parts,
+                                                                    int nslice) {
+    __shared__ Part sp[kStatThreads / 64];
+    const int slice = blockIdx.x, r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int rows = gridDim.y;
+    const float* z = row_ptr(a, b, r);
+    // slice bounds in float4 units (16-byte aligned rows with V % 4 == 0) or elements
+    const bool vec = (a.V & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0;
+    const int units = vec ? a.V / 4 : a.V;
+    const int per = (units + nslice - 1) / nslice;
+    const int u0 = slice * per, u1 = min(units, u0 + per);
+    const float it = a.inv_temp;
+    float m = kNegInf, s = 0.f, best = kNegInf;
+    int bi = 0x7fffffff;
+    auto visit = [&](float zv, int x) {
+        if (zv > best) { best = zv; bi = x; }      // each thread visits increasing x
+        if constexpr (!GREEDY) {
+            const float y = zv * it;
+            if (y > m) { s = s * __expf(m - y) + 1.f; m = y; }
+            else s += __expf(y - m);
+        }
+    };
+    if (vec) {
+        const float4* z4 = reinterpret_cast<const float4*>(z);
+        int j = u0 + tid;
+        for (; j + 3 * kStatThreads < u1; j += 4 * kStatThreads) {
+            float4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = z4[j + q * kStatThreads];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int x = 4 * (j + q * kStatThreads);
+                visit(v[q].x, x); visit(v[q].y, x + 1); visit(v[q].z, x + 2); visit(v[q].w, x + 3);
+            }
+        }
+        for (; j < u1; j += kStatThreads) {
+            const float4 v = z4[j];
+            visit(v.x, 4 * j); visit(v.y, 4 * j + 1); visit(v.z, 4 * j + 2); visit(v.w, 4 * j + 3);
+        }
+    } else {
+        for (int j = u0 + tid; j < u1; j += kStatThreads) visit(z[j], j);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o), b2 = __shfl_xor(best, o);
+        const int i2 = __shfl_xor(bi, o);
+        if constexpr (!GREEDY) ms_merge(m, s, m2, s2);
+        am_merge(best, bi, b2, i2);
+    }
+    const int lane = tid & 63, wid = tid >> 6;
+    if (lane == 0) sp[wid] = Part{m, s, best, bi};
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < kStatThreads / 64; ++w) {
+            if constexpr (!GREEDY) ms_merge(m, s, sp[w].m, sp[w].s);
+            am_merge(best, bi, sp[w].zmax, sp[w].imax);
+        }
+        parts[(((size_t)b * rows) + r) * nslice + slice] = Part{m, s, best, bi};
+    }
+}
+
+// One wave per sequence: row statistics, accept walk, accepted prefix.
+__global__ __launch_bounds__(64) void accept_decide_kernel(AcceptArgs a, const Part* parts,
+                                                           int nslice, int rows,
+                                                           Decision* dec) {
+    __shared__ float st[64][4];
+    const int b = blockIdx.x, lane = threadIdx.x;
     const int gamma = a.gamma, V = a.V;
     const bool greedy = a.inv_temp == 0.f;
-    const float* st = a.stats + (size_t)b * (2 * gamma + 1) * 4;
-    const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
-    const uint32_t off = (uint32_t)a.offset;
-    int32_t* out = a.out_tokens + (size_t)b * (gamma + 1);
-
-    if (tid == 0) {
-        int n = 0;
-        for (; n < gamma; ++n) {
-            const int x = a.tokens[(size_t)b * gamma + n];
-            bool ok;
-            if (greedy) {
-                ok = (int)st[n * 4 + 3] == x;
-            } else {
-                const float* t = st + n * 4;
-                const float* d = st + (gamma + 1 + n) * 4;
-                const float p = __expf(t[2] - t[0]) / t[1];
-                const float q = __expf(d[2] - d[0]) / d[1];
-                uint32_t c0 = 0, c1 = (uint32_t)n, c2 = (uint32_t)b, c3 = off;
-                philox4x32_10(c0, c1, c2, c3, k0, k1);
-                ok = (x >= 0 && x < V) && philox_uniform(c0) < p / q;
-            }
-            if (!ok) break;
-            out[n] = x;
+    for (int r = lane; r < rows; r += 64) {
+        const Part* p = parts + ((size_t)b * rows + r) * nslice;
+        float m = kNegInf, s = 0.f, best = kNegInf;
+        int bi = 0x7fffffff;
+        for (int k = 0; k < nslice; ++k) {
+            if (!greedy) ms_merge(m, s, p[k].m, p[k].s);
+            am_merge(best, bi, p[k].zmax, p[k].imax);
         }
-        for (int j = n + 1; j <= gamma; ++j) out[j] = -1;
-        a.out_num[b] = n;
-        if (greedy) out[n] = (int)st[n * 4 + 3];
-        s_pos = n;
+        float zx = 0.f;
+        if (!greedy && r != gamma) {
+            const int i = (r < gamma) ? r : r - gamma - 1;
+            const int x = a.tokens[(size_t)b * gamma + i];
+            zx = (x >= 0 && x < V) ? row_ptr(a, b, r)[x] * a.inv_temp : kNegInf;
+        }
+        if (r < 64) { st[r][0] = m; st[r][1] = s; st[r][2] = zx; st[r][3] = (float)bi; }
+        if (a.stats != nullptr) {
+            float* o = a.stats + ((size_t)b * (2 * gamma + 1) + r) * 4;
+            o[0] = greedy ? 0.f : m;
+            o[1] = greedy ? 0.f : s;
+            o[2] = zx;
+            o[3] = (float)bi;
+        }
     }
-    if (greedy) return;
     __syncthreads();
+    if (lane != 0) return;
+    const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
+    int32_t* out = a.out_tokens + (size_t)b * (gamma + 1);
+    int n = 0;
+    for (; n < gamma; ++n) {
+        const int x = a.tokens[(size_t)b * gamma + n];
+        bool ok;
+        if (greedy) {
+            ok = (int)st[n][3] == x;
+        } else {
+            const float p = __expf(st[n][2] - st[n][0]) / st[n][1];
+            const float q = __expf(st[gamma + 1 + n][2] - st[gamma + 1 + n][0]) / st[gamma + 1 + n][1];
+            uint32_t c0 = 0, c1 = (uint32_t)n, c2 = (uint32_t)b, c3 = (uint32_t)a.offset;
+            philox4x32_10(c0, c1, c2, c3, k0, k1);
+            ok = (x >= 0 && x < V) && philox_uniform(c0) < p / q;
+        }
+        if (!ok) break;
+        out[n] = x;
+    }
+    for (int j = n + 1; j <= gamma; ++j) out[j] = -1;
+    a.out_num[b] = n;
+    if (greedy) out[n] = (int)st[n][3];
+    dec[b].pos = n;
+}
 
-    const int pos = s_pos;
+// Exponential race over one slice of the emitting row of one sequence.
+__global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a, const Part* parts,
+                                                                   int nslice, int rows,
+                                                                   const Decision* dec,
+                                                                   RaceKey* race, int nrace) {
+    __shared__ RaceKey sr[kRaceThreads / 64], sq[kRaceThreads / 64];
+    const int slice = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int gamma = a.gamma, V = a.V;
+    const int pos = dec[b].pos;
     const bool residual = pos < gamma;
+    // merged statistics of the two rows (identical arithmetic to the decide kernel)
+    float mt = kNegInf, st = 0.f, md = kNegInf, sd = 0.f;
+    {
+        const Part* pt = parts + ((size_t)b * rows + pos) * nslice;
+        for (int k = 0; k < nslice; ++k) ms_merge(mt, st, pt[k].m, pt[k].s);
+        if (residual) {
+            const Part* pd = parts + ((size_t)b * rows + gamma + 1 + pos) * nslice;
+            for (int k = 0; k < nslice; ++k) ms_merge(md, sd, pd[k].m, pd[k].s);
+        }
+    }
     const float* zt = a.target + ((size_t)b * (gamma + 1) + pos) * V;
     const float* zd = residual ? a.draft + ((size_t)b * gamma + pos) * V : nullptr;
-    const float* ts = st + pos * 4;
-    const float* ds = residual ? st + (gamma + 1 + pos) * 4 : nullptr;
-    const float it = a.inv_temp;
-    RaceKey br{__builtin_huge_valf(), 0x7fffffff}, bp{__builtin_huge_valf(), 0x7fffffff};
+    // p(x) = 2^(z(x) * it * log2e - m * log2e) / s, evaluated as one FMA and one v_exp.
+    const float c1 = a.inv_temp * kLog2e;
+    const float ct = mt * kLog2e, cd = md * kLog2e;
+    const float rst = 1.f / st, rsd = residual ? 1.f / sd : 0.f;
+    const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
+    const uint32_t off = (uint32_t)a.offset;
     const int nblk = (V + 3) / 4;
-    for (int j = tid; j < nblk; j += kRaceThreads) {
-        uint32_t w[4] = {(uint32_t)j, (1u << 16) | (uint32_t)pos, (uint32_t)b, off};
-        philox4x32_10(w[0], w[1], w[2], w[3], k0, k1);
+    const int per = (nblk + nrace - 1) / nrace;
+    const int j0 = slice * per, j1 = min(nblk, j0 + per);
+    RaceKey br{__builtin_huge_valf(), 0x7fffffff}, bp{__builtin_huge_valf(), 0x7fffffff};
+    for (int j = j0 + tid; j < j1; j += kRaceThreads) {
+        uint32_t w0 = (uint32_t)j, w1 = (1u << 16) | (uint32_t)pos, w2 = (uint32_t)b, w3 = off;
+        philox4x32_10(w0, w1, w2, w3, k0, k1);
+        const uint32_t w[4] = {w0, w1, w2, w3};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int x = 4 * j + e;
             if (x >= V) break;
-            const float E = -__logf(philox_uniform(w[e]));
-            const float pt = __expf(zt[x] * it - ts[0]) / ts[1];
-            if (pt > 0.f) race_merge(bp, {E / pt, x});
+            const float E = -__builtin_amdgcn_logf(philox_uniform(w[e])) * kLn2;
+            const float pt = __builtin_amdgcn_exp2f(fmaf(zt[x], c1, -ct)) * rst;
+            if (pt > 0.f) race_merge(bp, {E * __builtin_amdgcn_rcpf(pt), x});
             if (residual) {
-                const float pd = __expf(zd[x] * it - ds[0]) / ds[1];
+                const float pd = __builtin_amdgcn_exp2f(fmaf(zd[x], c1, -cd)) * rsd;
                 const float rr = pt - pd;
-                if (rr > 0.f) race_merge(br, {E / rr, x});
+                if (rr > 0.f) race_merge(br, {E * __builtin_amdgcn_rcpf(rr), x});
             }
         }
     }
@@ -172,25 +231,61 @@ __global__ __launch_bounds__(kRaceThreads) void accept_decide_kernel(AcceptArgs 
         race_merge(bp, {__shfl_xor(bp.key, o), __shfl_xor(bp.x, o)});
     }
     const int lane = tid & 63, wid = tid >> 6;
-    if (lane == 0) { sr[wid] = br; sp[wid] = bp; }
+    if (lane == 0) { sr[wid] = br; sq[wid] = bp; }
     __syncthreads();
     if (tid == 0) {
-        for (int w = 1; w < kRaceThreads / 64; ++w) { race_merge(br, sr[w]); race_merge(bp, sp[w]); }
-        const bool use_r = residual && br.x != 0x7fffffff;
-        out[pos] = use_r ? br.x : bp.x;
+        for (int w = 1; w < kRaceThreads / 64; ++w) { race_merge(br, sr[w]); race_merge(bp, sq[w]); }
+        race[((size_t)b * nrace + slice) * 2 + 0] = br;
+        race[((size_t)b * nrace + slice) * 2 + 1] = bp;
     }
+}
+
+__global__ __launch_bounds__(64) void accept_finalize_kernel(AcceptArgs a, const Decision* dec,
+                                                             const RaceKey* race, int nrace) {
+    const int b = blockIdx.x;
+    if (threadIdx.x != 0) return;
+    RaceKey br{__builtin_huge_valf(), 0x7fffffff}, bp{__builtin_huge_valf(), 0x7fffffff};
+    for (int k = 0; k < nrace; ++k) {
+        race_merge(br, race[((size_t)b * nrace + k) * 2 + 0]);
+        race_merge(bp, race[((size_t)b * nrace + k) * 2 + 1]);
+    }
+    const int pos = dec[b].pos;
+    const bool use_r = pos < a.gamma && br.x != 0x7fffffff;
+    a.out_tokens[(size_t)b * (a.gamma + 1) + pos] = use_r ? br.x : bp.x;
 }
 
 }  // namespace
 
-hipError_t launch_accept(const AcceptArgs& a, hipStream_t s) {
+AcceptPlan accept_plan(int B, int gamma, int V) {
+    AcceptPlan p;
+    p.nslice = V >= 8192 ? (V + 16383) / 16384 : 1;
+    p.nrace = V >= 8192 ? (V + 8191) / 8192 : 1;
+    const size_t rows = (size_t)B * (2 * gamma + 1);
+    p.parts_bytes = rows * p.nslice * sizeof(Part);
+    p.dec_bytes = (size_t)B * sizeof(Decision);
+    p.race_bytes = (size_t)B * p.nrace * 2 * sizeof(RaceKey);
+    return p;
+}
+
+hipError_t launch_accept(const AcceptArgs& a, void* ws, hipStream_t s) {
     const bool greedy = a.inv_temp == 0.f;
     const int rows = greedy ? a.gamma + 1 : 2 * a.gamma + 1;
-    if (greedy) accept_stats_kernel<true><<<dim3(rows, a.B), kStatThreads, 0, s>>>(a);
-    else accept_stats_kernel<false><<<dim3(rows, a.B), kStatThreads, 0, s>>>(a);
+    const AcceptPlan p = accept_plan(a.B, a.gamma, a.V);
+    char* w = static_cast<char*>(ws);
+    Part* parts = reinterpret_cast<Part*>(w);
+    Decision* dec = reinterpret_cast<Decision*>(w + p.parts_bytes);
+    RaceKey* race = reinterpret_cast<RaceKey*>(w + p.parts_bytes + p.dec_bytes);
+    const dim3 sgrid(p.nslice, rows, a.B);
+    if (greedy) accept_stats_kernel<true><<<sgrid, kStatThreads, 0, s>>>(a, parts, p.nslice);
+    else accept_stats_kernel<false><<<sgrid, kStatThreads, 0, s>>>(a, parts, p.nslice);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    accept_decide_kernel<<<a.B, kRaceThreads, 0, s>>>(a);
+    accept_decide_kernel<<<a.B, 64, 0, s>>>(a, parts, p.nslice, rows, dec);
+    if ((e = hipGetLastError()) != hipSuccess || greedy) return e;
+    accept_race_kernel<<<dim3(p.nrace, a.B), kRaceThreads, 0, s>>>(a, parts, p.nslice, rows, dec,
+                                                                   race, p.nrace);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    accept_finalize_kernel<<<a.B, 64, 0, s>>>(a, dec, race, p.nrace);
     return hipGetLastError();
 }
 

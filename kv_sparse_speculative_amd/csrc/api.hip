@@ -43,6 +43,7 @@ long ceil_div(long a, long b) { return (a + b - 1) / b; }
 constexpr long kTargetWorkgroups = 1024;
 constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes per round
 constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
+constexpr int kMaxGamma = 31;      // speculation length limit of spec_accept
 
 struct Plan {
     int nsplit;
@@ -327,8 +328,9 @@ int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads, int w, 
 }
 
 size_t kvss_accept_workspace_bytes(int batch, int gamma, int vocab) {
-    if (batch < 0 || gamma < 0 || vocab <= 0) return 0;
-    return align_up((size_t)batch * (2 * gamma + 1) * 4 * sizeof(float));
+    if (batch < 0 || gamma < 0 || gamma > kMaxGamma || vocab <= 0) return 0;
+    const kvss::AcceptPlan p = kvss::accept_plan(batch, gamma, vocab);
+    return align_up(p.parts_bytes + p.dec_bytes + p.race_bytes);
 }
 
 int spec_accept(const float* target_logits, const float* draft_logits, const int32_t* draft_tokens,
@@ -336,7 +338,8 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
                 int32_t* out_tokens, int32_t* out_num_accepted, float* row_stats, void* workspace,
                 size_t workspace_bytes, void* stream) {
     if (batch < 0) return fail(KVSS_EINVAL, "batch must be >= 0");
-    if (gamma < 0 || gamma >= 65536) return fail(KVSS_EINVAL, "gamma must be in [0, 65536)");
+    if (gamma < 0) return fail(KVSS_EINVAL, "gamma must be >= 0");
+    if (gamma > kMaxGamma) return fail(KVSS_EUNSUPPORTED, "gamma %d exceeds %d", gamma, kMaxGamma);
     if (vocab <= 0 || vocab >= (1 << 24)) return fail(KVSS_EINVAL, "vocab must be in [1, 2^24)");
     if (!(temperature >= 0.f) || !isfinite(temperature))
         return fail(KVSS_EINVAL, "temperature must be finite and >= 0");
@@ -345,7 +348,7 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
         return fail(KVSS_EINVAL, "target_logits, draft_tokens, out_tokens, out_num_accepted must be non-NULL");
     if (temperature > 0.f && gamma > 0 && !draft_logits)
         return fail(KVSS_EINVAL, "draft_logits must be non-NULL when temperature > 0");
-    const size_t need = row_stats ? 0 : kvss_accept_workspace_bytes(batch, gamma, vocab);
+    const size_t need = kvss_accept_workspace_bytes(batch, gamma, vocab);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                     workspace_bytes, need);
@@ -359,10 +362,11 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
     a.inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
     a.seed = seed;
     a.offset = offset;
-    a.stats = row_stats ? row_stats : static_cast<float*>(workspace);
+    a.stats = row_stats;
     a.out_tokens = out_tokens;
     a.out_num = out_num_accepted;
-    return hip_status(kvss::launch_accept(a, static_cast<hipStream_t>(stream)), "accept launch");
+    return hip_status(kvss::launch_accept(a, workspace, static_cast<hipStream_t>(stream)),
+                      "accept launch");
 }
 
 }  // extern "C"

@@ -71,11 +71,18 @@ struct AcceptArgs {
     int B, gamma, V;
     float inv_temp;             // 0 => greedy
     uint64_t seed, offset;
-    float* stats;               // [B, 2*gamma+1, 4]
+    float* stats;               // [B, 2*gamma+1, 4] or null
     int32_t* out_tokens;        // [B, gamma+1]
     int32_t* out_num;           // [B]
 };
 
-hipError_t launch_accept(const AcceptArgs& a, hipStream_t s);
+// Workspace carve-up of one acceptance call: per-row slice partials, per-sequence decisions,
+// per-sequence race partials.
+struct AcceptPlan {
+    int nslice, nrace;
+    size_t parts_bytes, dec_bytes, race_bytes;
+};
+AcceptPlan accept_plan(int B, int gamma, int V);
+hipError_t launch_accept(const AcceptArgs& a, void* workspace, hipStream_t s);
 
 }  // namespace kvss

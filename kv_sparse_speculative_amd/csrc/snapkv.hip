@@ -199,23 +199,39 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     }
     __syncthreads();
 
-    // Radix select (most significant byte first) of the k-th largest bit pattern.
+    // Radix select (most significant byte first) of the k-th largest bit pattern. Scores of
+    // one head share a few exponent values, so histogram increments are aggregated per wave:
+    // eight ballots give every lane the set of lanes holding the same digit, and the lowest of
+    // them adds the set's size -- one conflict-free LDS atomic per distinct digit.
+    const int lane = tid & 63;
     unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
+    const int n_pad = (n + 1023) / 1024 * 1024;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         for (int t = tid; t < 256; t += 1024) hist[t] = 0;
         __syncthreads();
-        for (int j = tid; j < n; j += 1024) {
-            const unsigned u = pl[j];
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        for (int j = tid; j < n_pad; j += 1024) {
+            const unsigned u = j < n ? pl[j] : 0u;
+            const bool match = j < n && (u & mask) == prefix;
+            const unsigned bin = (u >> shift) & 255u;
+            unsigned long long peers = __ballot(match);
+#pragma unroll
+            for (int bit = 0; bit < 8; ++bit) {
+                const bool set = (bin >> bit) & 1u;
+                const unsigned long long m = __ballot(set);
+                peers &= set ? m : ~m;
+            }
+            if (match && __ffsll((long long)peers) - 1 == lane)
+                atomicAdd(&hist[bin], (unsigned)__popcll(peers));
         }
         __syncthreads();
-        if (tid == 0) {
-            unsigned cum = 0;
-            for (int d = 255; d >= 0; --d) {
-                if (cum + hist[d] >= remaining) { s_digit = d; s_remaining = remaining - cum; break; }
-                cum += hist[d];
-            }
+        // Find the bin where the count from the top first reaches `remaining`.
+        const int cnt = tid < 256 ? (int)hist[255 - tid] : 0;
+        int tot;
+        const int above = block_scan_1024(cnt, sh, tot);
+        if (tid < 256 && above < (int)remaining && above + cnt >= (int)remaining) {
+            s_digit = 255 - tid;
+            s_remaining = remaining - above;
         }
         __syncthreads();
         prefix |= s_digit << shift;

@@ -245,7 +245,7 @@ def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, 
         n_acc = torch.empty(B, dtype=torch.int32, device=dev)
     if row_stats is None and want_stats:
         row_stats = torch.zeros((B, 2 * gamma + 1, 4), dtype=torch.float32, device=dev)
-    nbytes = 0 if row_stats is not None else lib().kvss_accept_workspace_bytes(B, gamma, V)
+    nbytes = lib().kvss_accept_workspace_bytes(B, gamma, V)
     workspace, wsb = _workspace(nbytes, workspace, dev)
     _check(lib().spec_accept(target_logits.data_ptr(), _ptr(draft_logits), draft_tokens.data_ptr(),
                              B, gamma, V, float(temperature), int(seed) & (2**64 - 1),

@@ -91,29 +91,32 @@ def rejection_accept_one(p_rows, q_rows, tokens, u_accept, race_u):
     return emitted, gamma
 
 
-def rejection_accept(target, draft, tokens, temperature, seed, offset):
+def rejection_accept(target, draft, tokens, temperature, seed, offset, seq_ids=None):
     """Rejection-sampling acceptance with Philox uniforms.
 
-    target [B, gamma + 1, V], draft [B, gamma, V] logits; tokens [B, gamma].
+    target [B, gamma + 1, V], draft [B, gamma, V] logits; tokens [B, gamma]. seq_ids gives the
+    batch index each row had in the full batch (it enters the Philox counter); default 0..B-1.
     """
     B, T, V = target.shape
     gamma = T - 1
+    ids = list(range(B)) if seq_ids is None else [int(x) for x in seq_ids]
     out = np.full((B, T), -1, dtype=np.int32)
     n_acc = np.zeros(B, dtype=np.int32)
     for b in range(B):
         p_rows = np.stack([softmax(target[b, i], temperature) for i in range(T)])
         q_rows = np.stack([softmax(draft[b, i], temperature) for i in range(gamma)])
+        sid = ids[b]
         emitted, n = rejection_accept_one(
             p_rows, q_rows, tokens[b],
-            lambda i, b=b: accept_uniform(seed, offset, b, i),
-            lambda i, b=b: race_uniforms(seed, offset, b, i, V))
+            lambda i, sid=sid: accept_uniform(seed, offset, sid, i),
+            lambda i, sid=sid: race_uniforms(seed, offset, sid, i, V))
         out[b, : len(emitted)] = emitted
         n_acc[b] = n
     return out, n_acc
 
 
-def spec_accept(target, draft, tokens, temperature, seed=0, offset=0):
+def spec_accept(target, draft, tokens, temperature, seed=0, offset=0, seq_ids=None):
     """Greedy when temperature == 0, rejection sampling otherwise."""
     if temperature == 0:
         return greedy_accept(target, tokens)
-    return rejection_accept(target, draft, tokens, temperature, seed, offset)
+    return rejection_accept(target, draft, tokens, temperature, seed, offset, seq_ids)
