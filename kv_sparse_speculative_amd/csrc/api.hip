@@ -41,6 +41,10 @@ long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 // Workgroups a launch should offer: 256 compute units, a few resident workgroups each.
 constexpr long kTargetWorkgroups = 1024;
+// Draft launches: one round of resident workgroups (two per CU).
+constexpr long kDraftTargetWorkgroups = 2 * 256;
+// The SnapKV row-statistics pass fits three workgroups per CU: aim at four full rounds.
+constexpr long kSnapTargetWorkgroups = 3 * 256 * 4;
 constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes per round
 constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
 constexpr int kMaxGamma = 31;      // speculation length limit of spec_accept
@@ -52,10 +56,11 @@ struct Plan {
 
 // Split a virtual key range of up to max_total keys per (sequence, KV head) so that the
 // launch offers about kTargetWorkgroups workgroups, each doing at least four rounds.
-Plan plan_splits(long pairs, long max_total, int unit, long max_len = 1L << 30) {
+Plan plan_splits(long pairs, long max_total, int unit, long max_len = 1L << 30,
+                 long target = kTargetWorkgroups) {
     Plan p{1, unit};
     if (max_total <= 0 || pairs <= 0) return p;
-    const long want = ceil_div(kTargetWorkgroups, pairs);
+    const long want = ceil_div(target, pairs);
     const long useful = ceil_div(max_total, 4L * unit);
     long ns = want < useful ? want : useful;
     if (ns < 1) ns = 1;
@@ -151,7 +156,8 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     // bf16 splits must fit one LDS table of block bases (kMfmaTableEntries - 1 blocks).
     s.p1 = kv->dtype == KVSS_BF16
                ? plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kMfmaUnit,
-                             (long)(kvss::kMfmaTableEntries - 1) * kv->block_size)
+                             (long)(kvss::kMfmaTableEntries - 1) * kv->block_size,
+                             kSnapTargetWorkgroups)
                : plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kSimpleUnit);
     s.n_stride = kv->max_kv_len > w ? kv->max_kv_len - w : 0;
     const size_t rows = (size_t)kv->batch * kv->num_kv_heads;
@@ -204,9 +210,12 @@ int verify_attn_full(const kvss_kv* kv, const void* q, int num_q_heads, int T, f
     return run_attention(a, p, false, kv->dtype, workspace, static_cast<hipStream_t>(stream));
 }
 
+// A draft set is short (hundreds to a few thousand keys): split only until every CU holds its
+// two resident single-row-tile workgroups; more splits add a merge launch and a second round.
 static Plan draft_plan(const kvss_kv* kv, int k_max, int max_tail) {
     return plan_splits((long)kv->batch * kv->num_kv_heads, (long)k_max + max_tail,
-                       kv->dtype == KVSS_BF16 ? kMfmaUnit : kSimpleUnit);
+                       kv->dtype == KVSS_BF16 ? kMfmaUnit : kSimpleUnit, 1L << 30,
+                       kDraftTargetWorkgroups);
 }
 
 size_t kvss_draft_workspace_bytes(const kvss_kv* kv, int num_q_heads, int k_max, int max_tail) {

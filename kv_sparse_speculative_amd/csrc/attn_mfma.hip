@@ -131,20 +131,28 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
             for (int base = 0; base < n; base += kTabUnroll * kWaves * 64) {
                 int pos[kTabUnroll];
                 bool ok[kTabUnroll];
+                // Reads are unconditional (indices clamped into range) so that all of a
+                // thread's selection reads, then all of its block-table reads, are in flight
+                // together.
+                int sv[kTabUnroll];
 #pragma unroll
                 for (int u = 0; u < kTabUnroll; ++u) {       // selection-list reads
                     const int v = seg + base + u * kWaves * 64 + tid;
-                    ok[u] = v < seg_end;
-                    pos[u] = lo + (v - n_list);
-                    if (ok[u] && v < n_list) {
-                        pos[u] = sel[v];
-                        ok[u] = pos[u] >= 0 && pos[u] < lo;
-                    }
+                    sv[u] = n_list > 0 ? sel[min(max(v, 0), n_list - 1)] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < kTabUnroll; ++u) {
+                    const int v = seg + base + u * kWaves * 64 + tid;
+                    const bool listed = v < n_list;
+                    pos[u] = listed ? sv[u] : lo + (v - n_list);
+                    ok[u] = v < seg_end && (!listed || (sv[u] >= 0 && sv[u] < lo));
                 }
                 int blk[kTabUnroll];
 #pragma unroll
-                for (int u = 0; u < kTabUnroll; ++u)         // block-table reads
-                    blk[u] = ok[u] ? btab[pos[u] / bs] : 0;
+                for (int u = 0; u < kTabUnroll; ++u) {       // block-table reads
+                    const int bi = ok[u] ? pos[u] / bs : 0;
+                    blk[u] = btab[bi];
+                }
 #pragma unroll
                 for (int u = 0; u < kTabUnroll; ++u) {
                     const int i = base + u * kWaves * 64 + tid;
@@ -301,21 +309,22 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
             wave_lds_order();
         };
 
-        // Double-buffered walk over this wave's chunks: chunk c+stride loads while c computes.
-        // Issues are unconditional (a chunk past the end loads a dummy row and is fully
-        // masked) so that every path reaches a consume with the same loads outstanding and
-        // the compiler's wait before it only covers the chunk being consumed.
+        // Double-buffered walk over this wave's chunks with two chunks always in flight:
+        // consume A, reissue A two chunks ahead, consume B, reissue B. Issues are
+        // unconditional (a chunk past the end loads a dummy row and is fully masked) and the
+        // loop condition is the only exit, so every consume is reached with the same loads
+        // outstanding and the compiler's wait covers only the chunk being consumed.
         constexpr int stride = kWaves * 32;
         uint4 kA[2][KS], vA[2][KS], kB[2][KS], vB[2][KS];
         unsigned okA[2], okB[2];
         int c = seg + wid * 32;
         issue(c, kA, vA, okA);
+        issue(c + stride, kB, vB, okB);
         for (; c < seg_end; c += 2 * stride) {
-            issue(c + stride, kB, vB, okB);
             consume(c, kA, vA, okA);
-            if (c + stride >= seg_end) break;
             issue(c + 2 * stride, kA, vA, okA);
             consume(c + stride, kB, vB, okB);
+            issue(c + 3 * stride, kB, vB, okB);
         }
     }
 

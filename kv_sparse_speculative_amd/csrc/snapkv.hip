@@ -260,6 +260,117 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     }
 }
 
+// Register-resident pool + top-k for up to 1024 * MAXC candidates (MAXC 16 or 32): thread t owns the
+// contiguous positions [t*C, t*C + C) and loads them once together with the pool halo, so the
+// radix passes and the ordered compaction touch registers only. Same selection rule as
+// snap_topk_kernel (centred max-pool, k largest by IEEE bits, ties to the lower position).
+constexpr int kPoolHalo = 3;   // register path: pool kernels up to 2 * kPoolHalo + 1
+
+template <int MAXC>
+__global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
+    __shared__ unsigned hist[256];
+    __shared__ int sh[16];
+    __shared__ unsigned s_digit, s_remaining;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
+    const int n = max(P - a.w, 0);
+    const int k = a.keep;
+    if (g == 0 && tid == 0) a.sel_count[b] = min(k, n);
+    int32_t* out = a.sel_idx + ((size_t)b * a.Hkv + g) * k;
+    if (n <= k) {
+        for (int j = tid; j < k; j += 1024) out[j] = j < n ? j : -1;
+        return;
+    }
+    const float* c = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
+    const int C = (n + 1023) / 1024;
+    const int base = tid * C;
+    const int r = a.pool / 2;
+    // window: win[q] = c[base - kPoolHalo + q]; -inf outside [0, n) and outside the halo
+    float win[MAXC + 2 * kPoolHalo];
+#pragma clang loop unroll(full)
+    for (int q = 0; q < MAXC + 2 * kPoolHalo; ++q) {
+        const int p = base - kPoolHalo + q;
+        const bool use = q >= kPoolHalo - r && q < kPoolHalo + C + r && p >= 0 && p < n;
+        win[q] = use ? c[p] : kNegInf;
+    }
+    // pooled value of position base + e overwrites win[e] (no later position reads it)
+#pragma clang loop unroll(full)
+    for (int e = 0; e < MAXC; ++e) {
+        float m = kNegInf;
+#pragma clang loop unroll(full)
+        for (int d = -kPoolHalo; d <= kPoolHalo; ++d)
+            if (d >= -r && d <= r) m = fmaxf(m, win[e + kPoolHalo + d]);
+        win[e] = m;
+    }
+    auto live = [&](int e) { return e < C && base + e < n; };
+
+    unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int t = tid; t < 256; t += 1024) hist[t] = 0;
+        __syncthreads();
+#pragma clang loop unroll(full)
+        for (int e = 0; e < MAXC; ++e) {
+            const unsigned u = __float_as_uint(win[e]);
+            const bool match = live(e) && (u & mask) == prefix;
+            const unsigned bin = (u >> shift) & 255u;
+            unsigned long long peers = __ballot(match);
+            if (peers == 0ull) continue;                   // no lane of the wave matches
+#pragma clang loop unroll(full)
+            for (int bit = 0; bit < 8; ++bit) {
+                const bool set = (bin >> bit) & 1u;
+                const unsigned long long mb = __ballot(set);
+                peers &= set ? mb : ~mb;
+            }
+            if (match && __ffsll((long long)peers) - 1 == lane)
+                atomicAdd(&hist[bin], (unsigned)__popcll(peers));
+        }
+        __syncthreads();
+        const int cnt = tid < 256 ? (int)hist[255 - tid] : 0;
+        int tot;
+        const int above = block_scan_1024(cnt, sh, tot);
+        if (tid < 256 && above < (int)remaining && above + cnt >= (int)remaining) {
+            s_digit = 255 - tid;
+            s_remaining = remaining - above;
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        mask |= 255u << shift;
+        remaining = s_remaining;
+        __syncthreads();
+    }
+    const unsigned thr = prefix;
+    int gt = 0, eq = 0;
+#pragma clang loop unroll(full)
+    for (int e = 0; e < MAXC; ++e) {
+        const unsigned u = __float_as_uint(win[e]);
+        gt += live(e) && u > thr;
+        eq += live(e) && u == thr;
+    }
+    int tot;
+    const int eq_before = block_scan_1024(eq, sh, tot);
+    int take = min(max((int)remaining - eq_before, 0), eq);
+    int pos = block_scan_1024(gt + take, sh, tot);
+#pragma clang loop unroll(full)
+    for (int e = 0; e < MAXC; ++e) {
+        const unsigned u = __float_as_uint(win[e]);
+        if (!live(e) || pos >= k) continue;
+        if (u > thr) out[pos++] = base + e;
+        else if (u == thr && take > 0) { out[pos++] = base + e; --take; }
+    }
+}
+
+hipError_t launch_topk(const SnapArgs& a, hipStream_t s) {
+    const dim3 grid(a.Hkv, a.B);
+    const int C = (a.n_stride + 1023) / 1024;
+    if (a.pool / 2 <= kPoolHalo) {
+        if (C <= 16) { snap_topk_reg_kernel<16><<<grid, 1024, 0, s>>>(a); return hipGetLastError(); }
+        if (C <= 32) { snap_topk_reg_kernel<32><<<grid, 1024, 0, s>>>(a); return hipGetLastError(); }
+    }
+    snap_topk_kernel<<<grid, 1024, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 template <typename ST, int D>
 hipError_t launch_typed(const SnapArgs& a, hipStream_t s) {
     snap_rowstats_kernel<ST, D><<<dim3(a.nsplit1, a.Hkv, a.B), 256, 0, s>>>(a);
@@ -270,8 +381,7 @@ hipError_t launch_typed(const SnapArgs& a, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    snap_topk_kernel<<<dim3(a.Hkv, a.B), 1024, 0, s>>>(a);
-    return hipGetLastError();
+    return launch_topk(a, s);
 }
 
 }  // namespace
@@ -281,8 +391,7 @@ hipError_t launch_snapkv(const SnapArgs& a, hipStream_t s) {
         // bf16: matrix-core score passes, then pool + top-k.
         hipError_t e = launch_snapkv_mfma_passes(a, s);
         if (e != hipSuccess) return e;
-        snap_topk_kernel<<<dim3(a.Hkv, a.B), 1024, 0, s>>>(a);
-        return hipGetLastError();
+        return launch_topk(a, s);
     }
     return a.D == 128 ? launch_typed<float, 128>(a, s) : launch_typed<float, 64>(a, s);
 }

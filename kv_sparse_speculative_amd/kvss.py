@@ -121,15 +121,16 @@ class PagedKV:
         self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = k.shape
         self.batch, self.max_blocks = block_table.shape
         self.dtype = k.dtype
+        self._desc = kvss_kv(k.data_ptr(), v.data_ptr(), block_table.data_ptr(),
+                             kv_lens.data_ptr(), self.batch, self.num_kv_heads, self.head_dim,
+                             self.block_size, self.max_blocks, self.num_blocks, self.max_kv_len,
+                             _DTYPE_CODE[self.dtype])
 
     def with_lens(self, kv_lens, max_kv_len):
         return PagedKV(self.k, self.v, self.block_table, kv_lens, max_kv_len)
 
     def desc(self):
-        return kvss_kv(self.k.data_ptr(), self.v.data_ptr(), self.block_table.data_ptr(),
-                       self.kv_lens.data_ptr(), self.batch, self.num_kv_heads, self.head_dim,
-                       self.block_size, self.max_blocks, self.num_blocks, self.max_kv_len,
-                       _DTYPE_CODE[self.dtype])
+        return self._desc
 
 
 def _workspace(nbytes, workspace, device):
