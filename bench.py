@@ -26,6 +26,104 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "KV-attn HBM GB/s (% peak) + verify/draft tokens/s, B=64 S=32000, 1 GPU"
+VERIFY_KERNEL = "attn_mfma_kernel<128, false, 2>"
+KERNEL_SOURCE = os.path.join(ROOT, "kv_sparse_speculative_amd", "csrc", "attn_mfma.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "verify_attn_llama8b_ctx32k_traffic.md")
+COPY_BYTES = 1 << 30          # plain copy used to calibrate the HBM byte counters
+
+
+def source_digest():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per verify launch from the committed counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel source sha256/16") != source_digest():
+        return None
+    try:
+        return int(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _read_csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True):
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, out_path, command):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the verify kernel and of the calibration
+    copy -> profiles summary with the copy-scaled HBM bytes per verify launch."""
+    def per_kernel(directory, counter):
+        vals = {}
+        for r in _read_csv_rows(directory, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    pick = lambda d, key: next((v for k, v in d.items() if key in k), None)
+    vf, vw = pick(fetch, VERIFY_KERNEL), pick(write, VERIFY_KERNEL)
+    # calibration copy: torch's device-to-device copy of COPY_BYTES runs as the runtime's blit
+    # kernel; its largest dispatches are the 1 GiB copies
+    cf = [v for k, v in fetch.items() if "copyBuffer" in k]
+    cw = [v for k, v in write.items() if "copyBuffer" in k]
+    cfk = max(max(v) for v in cf) if cf else None
+    cwk = max(max(v) for v in cw) if cw else None
+    f_scale = COPY_BYTES / (cfk * 1024) if cfk else None
+    w_scale = COPY_BYTES / (cwk * 1024) if cwk else None
+    mean = lambda v: sum(v) / len(v)
+    fetch_b = mean(vf) * 1024 * f_scale
+    write_b = mean(vw) * 1024 * w_scale
+    total = int(fetch_b + write_b)
+    lines = [
+        "# Verify attention (Llama-3.1-8B-shaped layer, B=64, context 32000, gamma 4): HBM traffic",
+        "",
+        "Counter runs (each counter in its own run), then this summary:",
+        "",
+        *[f"    {c}" for c in command],
+        "",
+        f"- kernel: `{VERIFY_KERNEL}`",
+        f"- kernel source sha256/16: `{source_digest()}`",
+        f"- FETCH_SIZE per dispatch (KiB, mean of {len(vf)}): {mean(vf):.1f}",
+        f"- WRITE_SIZE per dispatch (KiB, mean of {len(vw)}): {mean(vw):.1f}",
+        f"- calibration copy of {COPY_BYTES} B: FETCH_SIZE {cfk:.1f} KiB, WRITE_SIZE {cwk:.1f} KiB",
+        f"- scale factors (bytes / counter bytes): fetch {f_scale:.4f}, write {w_scale:.4f}",
+        f"- HBM bytes per launch: {total}",
+        f"- algorithmic bytes per launch: 8397824000",
+        f"- traffic / algorithmic: {total / 8397824000:.4f}",
+    ]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_stats(stats_dir, out_path, title, command):
+    """rocprofv3 --stats kernel table (kvss kernels) -> profiles summary."""
+    rows = _read_csv_rows(stats_dir, "kernel_stats.csv")
+    lines = [f"# {title}", "", "Command:", "", *[f"    {c}" for c in command], "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        if "kvss" not in r["Name"]:
+            continue
+        name = r["Name"].replace("kvss::(anonymous namespace)::", "").replace("(kvss::", "(")
+        lines.append(f"| `{name[:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def algorithmic_bytes(wl, P, T, sink, window, V):
@@ -127,7 +225,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="after timing, run a plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "OUT"))
+    ap.add_argument("--title", default="kvss kernels")
+    ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.command)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats, args.title, args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path is not sharded across GPUs (run with --gpus 1)",
               file=sys.stderr)
@@ -249,9 +359,16 @@ def main():
                    "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": D,
                    "snapkv_budget": budget, "streaming": [sink, window], "vocab": ns.vocab},
         "roofline": {"bound": "hbm", "achieved": v["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": v["frac_peak"], "traffic": None, "kernel": "verify_attn_full"},
+                     "frac": v["frac_peak"], "traffic": committed_traffic(),
+                     "kernel": "verify_attn_full"},
         "calls": detail,
     }
+    if args.copy_reference:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, ns, sink, window)
     print(json.dumps(result), flush=True)
