@@ -328,6 +328,20 @@ def main():
             per_call[c] += ev[i].elapsed_time(ev[i + 1]) / args.steps
     ms_step = wall * 1e3 / args.steps
 
+    # measured read ceiling: a plain stream over the K cache (after the timed region)
+    sink_buf = torch.zeros(1, dtype=torch.int32, device=dev)
+    rd = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kvss.kvss_stream_read(ns.k_cache, sink_buf)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rd.append(e0.elapsed_time(e1))
+    rd.sort()
+    stream_gbs = ns.k_cache.numel() * ns.k_cache.element_size() / (rd[2] * 1e-3) / 1e9
+
     nbytes = algorithmic_bytes(wl, P, T, sink, window, ns.vocab)
     total_bytes = sum(nbytes.values())
     detail = {}
@@ -335,7 +349,7 @@ def main():
         ms = per_call[c]
         gbs = nbytes[c] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
         d = {"ms": round(ms, 4), "GB_per_s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4),
-             "bytes": nbytes[c]}
+             "frac_stream": round(gbs / stream_gbs, 4), "bytes": nbytes[c]}
         if c == "verify":
             d["tokens_per_s"] = round(B * T / (ms * 1e-3), 1)
         if c.startswith("draft"):
@@ -362,6 +376,7 @@ def main():
                      "frac": v["frac_peak"], "traffic": committed_traffic(),
                      "kernel": "verify_attn_full"},
         "calls": detail,
+        "stream_read_GB_per_s": round(stream_gbs, 1),
     }
     if args.copy_reference:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)

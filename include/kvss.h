@@ -199,6 +199,14 @@ KVSS_API int spec_accept(const float* target_logits, const float* draft_logits,
                 uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
                 float* row_stats, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * kvss_stream_read -- measurement reference, not part of the method: reads `bytes` (rounded
+ * down to a multiple of 16) of the device buffer `src` (16-byte aligned) with 16-byte loads, the
+ * practical HBM read ceiling against which the attention kernels' bandwidth is also reported.
+ * `sink` is a device uint32 that is written only in a data-dependent corner case.
+ */
+KVSS_API int kvss_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

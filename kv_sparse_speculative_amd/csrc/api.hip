@@ -378,4 +378,13 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
                       "accept launch");
 }
 
+int kvss_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (bytes == 0) return ok();
+    if (!src || !sink) return fail(KVSS_EINVAL, "src and sink must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(src) % 16 != 0)
+        return fail(KVSS_EINVAL, "src must be 16-byte aligned");
+    return hip_status(kvss::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)),
+                      "stream read launch");
+}
+
 }  // extern "C"

@@ -85,4 +85,6 @@ struct AcceptPlan {
 AcceptPlan accept_plan(int B, int gamma, int V);
 hipError_t launch_accept(const AcceptArgs& a, void* workspace, hipStream_t s);
 
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace kvss

@@ -260,18 +260,26 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     }
 }
 
-// Register-resident pool + top-k for up to 1024 * MAXC candidates (MAXC 16 or 32): thread t owns the
-// contiguous positions [t*C, t*C + C) and loads them once together with the pool halo, so the
-// radix passes and the ordered compaction touch registers only. Same selection rule as
-// snap_topk_kernel (centred max-pool, k largest by IEEE bits, ties to the lower position).
+// Register-resident pool + top-k for up to 1024 * MAXC candidates (MAXC 16 or 32), same
+// selection rule as snap_topk_kernel (centred max-pool, k largest by IEEE bits, ties to the
+// lower position, ascending output):
+//   1. the scores of one (sequence, KV head) are read once, coalesced, into LDS (one pad word
+//      per 32 so that reading a thread's contiguous run is conflict-free);
+//   2. thread t takes the contiguous positions [t*C, t*C + C) plus the pool halo from LDS and
+//      keeps the pooled values in registers;
+//   3. four MSB-first radix passes count digits into per-wave LDS histograms (no cross-wave
+//      contention) and pick the digit of the k-th largest with one block scan;
+//   4. an ordered compaction writes the kept positions.
 constexpr int kPoolHalo = 3;   // register path: pool kernels up to 2 * kPoolHalo + 1
+constexpr int kTopkWaves = 16;
+constexpr size_t kTopkMaxLds = 150 * 1024;  // dynamic LDS of the register path (of 160 KB)
 
 template <int MAXC>
 __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
-    __shared__ unsigned hist[256];
+    extern __shared__ float lds_scores[];            // n + n/32 floats, then histograms
     __shared__ int sh[16];
     __shared__ unsigned s_digit, s_remaining;
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wid = tid >> 6;
     const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
     const int n = max(P - a.w, 0);
     const int k = a.keep;
@@ -282,16 +290,18 @@ __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
         return;
     }
     const float* c = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
+    for (int j = tid; j < n; j += 1024) lds_scores[j + (j >> 5)] = c[j];
+    __syncthreads();
+
     const int C = (n + 1023) / 1024;
     const int base = tid * C;
     const int r = a.pool / 2;
-    // window: win[q] = c[base - kPoolHalo + q]; -inf outside [0, n) and outside the halo
     float win[MAXC + 2 * kPoolHalo];
 #pragma clang loop unroll(full)
     for (int q = 0; q < MAXC + 2 * kPoolHalo; ++q) {
         const int p = base - kPoolHalo + q;
         const bool use = q >= kPoolHalo - r && q < kPoolHalo + C + r && p >= 0 && p < n;
-        win[q] = use ? c[p] : kNegInf;
+        win[q] = use ? lds_scores[p + (p >> 5)] : kNegInf;
     }
     // pooled value of position base + e overwrites win[e] (no later position reads it)
 #pragma clang loop unroll(full)
@@ -303,30 +313,24 @@ __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
         win[e] = m;
     }
     auto live = [&](int e) { return e < C && base + e < n; };
+    __syncthreads();                                  // the score staging area is reused below
+    unsigned* whist = reinterpret_cast<unsigned*>(lds_scores);      // [kTopkWaves][256]
 
     unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int t = tid; t < 256; t += 1024) hist[t] = 0;
+        for (int t = tid; t < kTopkWaves * 256; t += 1024) whist[t] = 0;
         __syncthreads();
 #pragma clang loop unroll(full)
         for (int e = 0; e < MAXC; ++e) {
             const unsigned u = __float_as_uint(win[e]);
-            const bool match = live(e) && (u & mask) == prefix;
-            const unsigned bin = (u >> shift) & 255u;
-            unsigned long long peers = __ballot(match);
-            if (peers == 0ull) continue;                   // no lane of the wave matches
-#pragma clang loop unroll(full)
-            for (int bit = 0; bit < 8; ++bit) {
-                const bool set = (bin >> bit) & 1u;
-                const unsigned long long mb = __ballot(set);
-                peers &= set ? mb : ~mb;
-            }
-            if (match && __ffsll((long long)peers) - 1 == lane)
-                atomicAdd(&hist[bin], (unsigned)__popcll(peers));
+            if (live(e) && (u & mask) == prefix) atomicAdd(&whist[wid * 256 + ((u >> shift) & 255u)], 1u);
         }
         __syncthreads();
-        const int cnt = tid < 256 ? (int)hist[255 - tid] : 0;
+        int cnt = 0;
+        if (tid < 256) {
+            for (int w = 0; w < kTopkWaves; ++w) cnt += whist[w * 256 + (255 - tid)];
+        }
         int tot;
         const int above = block_scan_1024(cnt, sh, tot);
         if (tid < 256 && above < (int)remaining && above + cnt >= (int)remaining) {
@@ -360,12 +364,33 @@ __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
     }
 }
 
+// LDS of the register path: padded scores (>= the per-wave histograms).
+size_t topk_reg_smem(int n_stride) {
+    const size_t scores = (size_t)(n_stride + n_stride / 32 + 1) * 4;
+    const size_t hist = (size_t)kTopkWaves * 256 * 4;
+    return scores > hist ? scores : hist;
+}
+
 hipError_t launch_topk(const SnapArgs& a, hipStream_t s) {
     const dim3 grid(a.Hkv, a.B);
     const int C = (a.n_stride + 1023) / 1024;
-    if (a.pool / 2 <= kPoolHalo) {
-        if (C <= 16) { snap_topk_reg_kernel<16><<<grid, 1024, 0, s>>>(a); return hipGetLastError(); }
-        if (C <= 32) { snap_topk_reg_kernel<32><<<grid, 1024, 0, s>>>(a); return hipGetLastError(); }
+    const size_t smem = topk_reg_smem(a.n_stride);
+    if (a.pool / 2 <= kPoolHalo && smem <= kTopkMaxLds) {
+        // dynamic LDS beyond the default 64 KB must be allowed per kernel
+        if (C <= 16) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&snap_topk_reg_kernel<16>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (e != hipSuccess) return e;
+            snap_topk_reg_kernel<16><<<grid, 1024, smem, s>>>(a);
+            return hipGetLastError();
+        }
+        if (C <= 32) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&snap_topk_reg_kernel<32>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (e != hipSuccess) return e;
+            snap_topk_reg_kernel<32><<<grid, 1024, smem, s>>>(a);
+            return hipGetLastError();
+        }
     }
     snap_topk_kernel<<<grid, 1024, 0, s>>>(a);
     return hipGetLastError();

@@ -56,6 +56,7 @@ _SIGNATURES = {
     "snapkv_select": (_I, [_KV, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _Z, _P]),
     "kvss_accept_workspace_bytes": (_Z, [_I, _I, _I]),
     "spec_accept": (_I, [_P, _P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _Z, _P]),
+    "kvss_stream_read": (_I, [_P, _Z, _P, _P]),
 }
 
 _lib = None
@@ -253,3 +254,11 @@ def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, 
                              int(offset) & (2**64 - 1), out_tokens.data_ptr(), n_acc.data_ptr(),
                              _ptr(row_stats), _ptr(workspace), wsb, _stream(stream)))
     return out_tokens, n_acc, row_stats
+
+
+def kvss_stream_read(buf, sink, stream=None):
+    """Measurement reference: stream-read every byte of the device tensor `buf`."""
+    _need(buf, "buf")
+    _need(sink, "sink")
+    _check(lib().kvss_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                  _stream(stream)))
