@@ -33,8 +33,16 @@ COPY_BYTES = 1 << 30          # plain copy used to calibrate the HBM byte counte
 
 
 def source_digest():
+    """Digest of what decides the verify kernel's code: its source, the headers it includes and
+    the compiler flags."""
     import hashlib
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    from kv_sparse_speculative_amd import build as kbuild
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "common.h"),
+                 os.path.join(os.path.dirname(KERNEL_SOURCE), "launch.h")):
+        h.update(open(path, "rb").read())
+    h.update(" ".join(kbuild.HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic():

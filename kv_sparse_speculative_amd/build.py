@@ -15,6 +15,8 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results land in ordinary VGPRs (no accumulator-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

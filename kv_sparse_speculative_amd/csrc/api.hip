@@ -153,10 +153,10 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     SnapLayout s{};
     const int G = num_q_heads / kv->num_kv_heads;
     s.R = G * w;
-    // bf16 splits must fit one LDS table of block bases (kMfmaTableEntries - 1 blocks).
+    // bf16 splits must fit one LDS table of block bases (kSnapTableEntries - 1 blocks).
     s.p1 = kv->dtype == KVSS_BF16
                ? plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kMfmaUnit,
-                             (long)(kvss::kMfmaTableEntries - 1) * kv->block_size,
+                             (long)(kvss::kSnapTableEntries - 1) * kv->block_size,
                              kSnapTargetWorkgroups)
                : plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kSimpleUnit);
     s.n_stride = kv->max_kv_len > w ? kv->max_kv_len - w : 0;

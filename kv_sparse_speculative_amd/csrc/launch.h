@@ -11,7 +11,8 @@ namespace kvss {
 constexpr int kMfmaTableEntries = 4096;
 
 // Candidate keys one workgroup of the bf16 SnapKV column-score pass covers.
-constexpr int kSnapColKeys = 2048;
+constexpr int kSnapColKeys = 4096;
+constexpr int kSnapTableEntries = 1024;     // block bases per SnapKV row-statistics split
 
 // One attention launch: R = G * T query rows per (sequence, KV head) over a key set that is
 // either the dense causal range [0, L) (verify) or a gathered list + dense tail (draft).

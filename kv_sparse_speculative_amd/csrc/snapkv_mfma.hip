@@ -16,6 +16,13 @@
 //           one key column, so the column sum is an in-lane sum plus one cross-group reduction.
 // Scores use scale * log2(e) in float32 after the bf16 contraction; statistics are kept in the
 // log2 domain. Partials are written per split; pass 2 merges them per row in its prologue.
+// A negative scale is folded into the staged queries (a bf16 sign flip is exact), so the
+// kernels only ever multiply by |scale| and the row maximum can be taken before scaling.
+// The hot loops are branch-free per lane: every 16-key tile lies in one cache block (splits and
+// tiles start on multiples of 16 and the block size is a multiple of 16), so its block lookup
+// is wave-uniform.
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -38,6 +45,7 @@ template <int D>
 __device__ void stage_queries(const SnapArgs& a, int b, int g, int NT, uint4* qs) {
     constexpr int KS = D / 32;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q_obs);
+    const unsigned flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
     for (int e = threadIdx.x; e < NT * KS * 64; e += kW * 64) {
         const int lane = e & 63, ks = (e >> 6) % KS, t = (e >> 6) / KS;
         const int r = t * 16 + (lane & 15);
@@ -46,6 +54,7 @@ __device__ void stage_queries(const SnapArgs& a, int b, int g, int NT, uint4* qs
             const int h = g * a.G + r / a.w, i = r % a.w;
             v = *reinterpret_cast<const uint4*>(qp + (((size_t)b * a.Hq + h) * a.w + i) * D +
                                                 ks * 32 + (lane >> 4) * 8);
+            v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
         }
         qs[e] = v;
     }
@@ -67,22 +76,24 @@ __device__ bool stage_blocks(const SnapArgs& a, int b, int g, int k0, int k1, un
     return bad;
 }
 
+// x / bs with a shift when the block size is a power of two (sh >= 0), else a division.
+__device__ __forceinline__ int div_bs(int x, int bs, int sh) { return sh >= 0 ? x >> sh : x / bs; }
+
 // Load the K rows of one 32-key chunk (keys c0 .. c0+31, each 16 lanes x 16 B) into registers.
-// Keys outside [k0, k1) or with a bad block load row 0 and are reported as masked.
+// c0 is wave-uniform and a multiple of 16, so each 16-key tile's block base is one uniform LDS
+// read. Keys outside [k0, k1) or with a bad block load row 0 and are reported as masked.
 template <int D>
-__device__ __forceinline__ void load_k(const uint16_t* kp, const unsigned* tab, int bs, int blk0,
-                                       int c0, int k1, int m16, int q4, uint4 (&kr)[2][D / 32],
-                                       unsigned (&okm)[2]) {
+__device__ __forceinline__ void load_k(const uint16_t* kp, const unsigned* tab, int bs, int sh,
+                                       int blk0, int c0, int k1, int m16, int q4,
+                                       uint4 (&kr)[2][D / 32], unsigned (&okm)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-        const int v = c0 + kt * 16 + m16;
-        unsigned row = kBadRow;
-        if (v < k1) {
-            const unsigned base = tab[v / bs - blk0];
-            row = base == kBadRow ? kBadRow : base + (unsigned)(v % bs);
-        }
-        const bool ok = row != kBadRow;
+        const int t0 = c0 + kt * 16;
+        unsigned base = kBadRow;
+        if (t0 < k1) base = tab[div_bs(t0, bs, sh) - blk0];
+        const bool ok = base != kBadRow && t0 + m16 < k1;
         okm[kt] = (unsigned)(__ballot(ok) & 0xffffull);
+        const unsigned row = base + (unsigned)(t0 - div_bs(t0, bs, sh) * bs + m16);
         const size_t off = (size_t)(ok ? row : 0u) * D + q4 * 8;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
@@ -90,135 +101,191 @@ __device__ __forceinline__ void load_k(const uint16_t* kp, const unsigned* tab, 
     }
 }
 
-template <int D, int NTMAX>
-struct SnapCfg {
-    static constexpr int KS = D / 32;
-    static constexpr int QS = NTMAX * KS * 64 * 16;               // NTMAX row tiles of queries
-    static constexpr int TAB = (kMfmaTableEntries + 1) * 4;
-};
+// One 16-row tile of the score product for 32 keys (two 16-key tiles), chained over D.
+// ROWS_A: queries are the A operand (S = Q . K^T, pass 2); else keys are (S^T = K . Q^T, pass 1).
+template <int KS, bool ROWS_A>
+__device__ __forceinline__ void score_tile(const uint4 (&qv)[KS], const uint4 (&kr)[2][KS],
+                                           f32x4 (&acc)[2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+            acc[kt] = ROWS_A
+                ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(qv[ks]), to_bf16x8(kr[kt][ks]), acc[kt], 0, 0, 0)
+                : __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(kr[kt][ks]), to_bf16x8(qv[ks]), acc[kt], 0, 0, 0);
+}
+
+template <int KS>
+__device__ __forceinline__ void read_q(const uint4* qs, int t, int lane, uint4 (&qv)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qv[ks] = qs[(t * KS + ks) * 64 + lane];
+}
 
 // ---------------------------------------------------------------- pass 1: row statistics
-template <int D, int NTMAX>
+// NT row tiles (16 rows each, rows past R are zero queries whose statistics are not written).
+template <int D, int NT>
 __global__ __launch_bounds__(kW * 64) void snap_rowstats_mfma(SnapArgs a) {
-    using C = SnapCfg<D, NTMAX>;
-    constexpr int KS = C::KS;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::QS + C::TAB];
-    __shared__ float sm[kW][NTMAX * 16], sl[kW][NTMAX * 16];
+    constexpr int KS = D / 32;
+    constexpr int QS = NT * KS * 64 * 16;                  // queries in MFMA operand order
+    constexpr int MS = 2 * kW * NT * 16 * 4;               // per-wave (max, sum), after the loop
+    constexpr int TAB = (kSnapTableEntries + 1) * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[(QS > MS ? QS : MS) + TAB];
     __shared__ int s_bad;
     uint4* qs = reinterpret_cast<uint4*>(smem);
-    unsigned* tab = reinterpret_cast<unsigned*>(smem + C::QS);
+    float* sm = reinterpret_cast<float*>(smem);             // [kW][NT*16], reuses the queries
+    float* sl = sm + kW * NT * 16;
+    unsigned* tab = reinterpret_cast<unsigned*>(smem + (QS > MS ? QS : MS));
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m16 = lane & 15, q4 = lane >> 4;
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
-    const int NT = (a.R + 15) / 16;
     const int k0 = split * a.split_len1;
     const int k1 = (split == a.nsplit1 - 1) ? P : min(k0 + a.split_len1, P);
-    if (tid == 0) s_bad = 0;
-    stage_queries<D>(a, b, g, NT, qs);
-    __syncthreads();
-    const int blk0 = k0 / a.bs;
+    const int bs = a.bs, sh = (bs & (bs - 1)) == 0 ? __builtin_ctz(bs) : -1;
+    const int blk0 = div_bs(k0, bs, sh);
     // The planner keeps a split within one table; a longer one is refused (poisoned, not read).
-    const bool fits = (k1 - k0) <= (kMfmaTableEntries - 1) * a.bs;
-    if (fits) {
-        if (stage_blocks(a, b, g, k0, k1, tab)) s_bad = 1;
-    } else if (tid == 0) {
-        s_bad = 1;
-    }
+    const bool fits = (k1 - k0) <= (kSnapTableEntries - 1) * bs;
+    if (tid == 0) s_bad = fits ? 0 : 1;
+    __syncthreads();
+    if (fits && stage_blocks(a, b, g, k0, k1, tab)) s_bad = 1;
     const int kend = fits ? k1 : k0;
     __syncthreads();
 
-    // Per lane: online (max, sum) of the scores it holds for row t*16 + m16, tile t < NT.
-    float mr[NTMAX], lr[NTMAX];
-#pragma unroll
-    for (int t = 0; t < NTMAX; ++t) { mr[t] = kNegInf; lr[t] = 0.f; }
-    // Causal bound of row r: P - w + (r % w).
-    int lim[NTMAX];
-#pragma unroll
-    for (int t = 0; t < NTMAX; ++t) lim[t] = P - a.w + ((t * 16 + m16) % a.w);
-
+    // The first two chunks are in flight while the queries are staged.
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
-    const int causal_from = P - a.w;            // keys below it are visible to every row
-
-    auto consume = [&](int c0, uint4 (&kr)[2][KS], unsigned (&okm)[2]) {
-        const bool full = (okm[0] & okm[1]) == 0xffffu && c0 + 31 < causal_from;
-#pragma unroll
-        for (int t = 0; t < NTMAX; ++t) {
-            if (t >= NT) break;
-            uint4 qb[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qb[ks] = qs[(t * KS + ks) * 64 + lane];
-            float sv[8];
-            float cmax = kNegInf;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(kr[kt][ks]),
-                                                                 to_bf16x8(qb[ks]), acc, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = acc[i] * a.scale_log2;
-                    if (!full) {
-                        const int key = kt * 16 + q4 * 4 + i;
-                        const bool ok = ((okm[kt] >> (q4 * 4 + i)) & 1u) && (c0 + key <= lim[t]);
-                        x = ok ? x : kNegInf;
-                    }
-                    sv[kt * 4 + i] = x;
-                    cmax = fmaxf(cmax, x);
-                }
-            }
-            const float mnew = fmaxf(mr[t], cmax);
-            if (mnew != kNegInf) {
-                float s = lr[t] * __builtin_amdgcn_exp2f(mr[t] - mnew);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) s += __builtin_amdgcn_exp2f(sv[j] - mnew);
-                lr[t] = s;
-                mr[t] = mnew;
-            }
-        }
-    };
-
     constexpr int stride = kW * 32;
     uint4 kA[2][KS], kB[2][KS];
     unsigned okA[2], okB[2];
     int c = k0 + wid * 32;
-    load_k<D>(kp, tab, a.bs, blk0, c, kend, m16, q4, kA, okA);
+    load_k<D>(kp, tab, bs, sh, blk0, c, kend, m16, q4, kA, okA);
+    load_k<D>(kp, tab, bs, sh, blk0, c + stride, kend, m16, q4, kB, okB);
+    stage_queries<D>(a, b, g, NT, qs);
+    __syncthreads();
+
+    // Per lane: online (max, sum) of the scores it holds for row t*16 + m16; the maximum is
+    // kept negated (nm = -m) so the exponent is one fma.
+    float nm[NT], lr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) { nm[t] = -kNegInf; lr[t] = 0.f; }
+    const float sc = fabsf(a.scale_log2);
+    const int causal_from = P - a.w;            // keys below it are visible to every row
+
+    // Tile t+1's products are issued before tile t's exponentials, so the matrix core and the
+    // vector ALU overlap within the wave.
+    auto consume = [&](auto full_tag, int c0, const uint4 (&kr)[2][KS], const unsigned (&okm)[2]) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        uint4 qv[2][KS];
+        f32x4 acc[2][2];
+        read_q<KS>(qs, 0, lane, qv[0]);
+        read_q<KS>(qs, 1, lane, qv[1]);
+        score_tile<KS, false>(qv[0], kr, acc[0]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            // Issue order per tile: the next tile's products, the queries two tiles ahead (into
+            // the registers this tile's products no longer need), then this tile's statistics.
+            if (t + 1 < NT) score_tile<KS, false>(qv[(t + 1) & 1], kr, acc[(t + 1) & 1]);
+            if (t + 2 < NT) read_q<KS>(qs, t + 2, lane, qv[t & 1]);
+            const f32x4* s = acc[t & 1];
+            if constexpr (FULL) {
+                // Lazy maximum: the reference -nm[t] moves only when a term could overflow the
+                // sum, i.e. when some score exceeds it by more than 64 (the tile sum then
+                // exceeds 2^64; at the start nm[t] = +inf makes it infinite).
+                float p = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p += __builtin_amdgcn_exp2f(fmaf(s[kt][i], sc, nm[t]));
+                const bool big = !(p <= 0x1p64f);
+                if (__ballot(big) != 0ull) {
+                    if (big) {
+                        // sc >= 0, so the maximum of the raw products scales to the score maximum.
+                        const float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                        const float mnew = fmaxf(-nm[t], cm * sc);
+                        lr[t] *= __builtin_amdgcn_exp2f(-nm[t] - mnew);
+                        p = 0.f;
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) p += __builtin_amdgcn_exp2f(fmaf(s[kt][i], sc, -mnew));
+                        nm[t] = -mnew;
+                    }
+                }
+                lr[t] += p;
+            } else {
+                const int lim = causal_from + ((t * 16 + m16) % a.w);   // causal bound of the row
+                float x[8];
+                float cm = kNegInf;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = kt * 16 + q4 * 4 + i;
+                        const bool ok = ((okm[kt] >> (q4 * 4 + i)) & 1u) && (c0 + key <= lim);
+                        x[kt * 4 + i] = ok ? s[kt][i] * sc : kNegInf;
+                        cm = fmaxf(cm, x[kt * 4 + i]);
+                    }
+                const float mold = -nm[t];
+                const float mnew = fmaxf(mold, cm);
+                const float ms = mnew == kNegInf ? 0.f : mnew;    // no key yet: every term is 0
+                float sum = lr[t] * __builtin_amdgcn_exp2f(mold - ms);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sum += __builtin_amdgcn_exp2f(x[j] - ms);
+                lr[t] = sum;
+                nm[t] = -mnew;
+            }
+            __builtin_amdgcn_sched_barrier(0);      // keep the per-tile issue order
+        }
+    };
+    auto step = [&](int c0, const uint4 (&kr)[2][KS], const unsigned (&okm)[2]) {
+        // Uniform: every key of the chunk is valid and visible to every row.
+        if ((okm[0] & okm[1]) == 0xffffu && c0 + 31 < causal_from)
+            consume(std::true_type{}, c0, kr, okm);
+        else
+            consume(std::false_type{}, c0, kr, okm);
+    };
+
+    // Two chunks in flight per wave: consume one, then reissue its registers two chunks ahead.
     for (; c < kend; c += 2 * stride) {
-        load_k<D>(kp, tab, a.bs, blk0, c + stride, kend, m16, q4, kB, okB);
-        consume(c, kA, okA);
+        step(c, kA, okA);
+        load_k<D>(kp, tab, bs, sh, blk0, c + 2 * stride, kend, m16, q4, kA, okA);
         if (c + stride >= kend) break;
-        load_k<D>(kp, tab, a.bs, blk0, c + 2 * stride, kend, m16, q4, kA, okA);
-        consume(c + stride, kB, okB);
+        step(c + stride, kB, okB);
+        load_k<D>(kp, tab, bs, sh, blk0, c + 3 * stride, kend, m16, q4, kB, okB);
     }
 
     // Merge the 4 lane groups (xor 16, 32) and then the waves, per row.
 #pragma unroll
-    for (int t = 0; t < NTMAX; ++t) {
-        if (t >= NT) break;
+    for (int t = 0; t < NT; ++t) {
+        float mr = -nm[t];
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
-            const float m2 = __shfl_xor(mr[t], o), l2 = __shfl_xor(lr[t], o);
-            const float M = fmaxf(mr[t], m2);
-            if (M != kNegInf) {
-                lr[t] = lr[t] * __builtin_amdgcn_exp2f(mr[t] - M) + l2 * __builtin_amdgcn_exp2f(m2 - M);
-                mr[t] = M;
-            }
+            const float m2 = __shfl_xor(mr, o), l2 = __shfl_xor(lr[t], o);
+            const float M = fmaxf(mr, m2);
+            const float Ms = M == kNegInf ? 0.f : M;
+            lr[t] = lr[t] * __builtin_amdgcn_exp2f(mr - Ms) + l2 * __builtin_amdgcn_exp2f(m2 - Ms);
+            mr = M;
         }
-        if (q4 == 0) { sm[wid][t * 16 + m16] = mr[t]; sl[wid][t * 16 + m16] = lr[t]; }
+        nm[t] = -mr;
     }
+    __syncthreads();                                        // every wave is done with the queries
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        if (q4 == 0) { sm[wid * NT * 16 + t * 16 + m16] = -nm[t]; sl[wid * NT * 16 + t * 16 + m16] = lr[t]; }
     __syncthreads();
     const bool poisoned = s_bad != 0;
     for (int r = tid; r < a.R; r += kW * 64) {
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kW; ++w) M = fmaxf(M, sm[w][r]);
+        for (int w = 0; w < kW; ++w) M = fmaxf(M, sm[w * NT * 16 + r]);
         float L = 0.f;
         if (M != kNegInf)
 #pragma unroll
-            for (int w = 0; w < kW; ++w) L += sl[w][r] * __builtin_amdgcn_exp2f(sm[w][r] - M);
+            for (int w = 0; w < kW; ++w) L += sl[w * NT * 16 + r] * __builtin_amdgcn_exp2f(sm[w * NT * 16 + r] - M);
         float* pp = a.part1 + ((((size_t)b * a.Hkv + g) * a.R + r) * a.nsplit1 + split) * 2;
         pp[0] = poisoned ? __builtin_nanf("") : M;
         pp[1] = poisoned ? __builtin_nanf("") : L;
@@ -226,18 +293,19 @@ __global__ __launch_bounds__(kW * 64) void snap_rowstats_mfma(SnapArgs a) {
 }
 
 // ---------------------------------------------------------------- pass 2: column scores
-template <int D, int NTMAX>
+template <int D, int NT>
 __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
-    using C = SnapCfg<D, NTMAX>;
-    constexpr int KS = C::KS;
+    constexpr int KS = D / 32;
+    constexpr int QS = NT * KS * 64 * 16;
     constexpr int TAB = (kSnapColKeys / 16 + 2) * 4;        // block bases of kSnapColKeys keys
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::QS + TAB];
-    __shared__ __attribute__((aligned(16))) float rowc[NTMAX * 16];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[QS + TAB];
+    __shared__ __attribute__((aligned(16))) float rowc[NT * 16];
     __shared__ int s_bad;
     uint4* qs = reinterpret_cast<uint4*>(smem);
-    unsigned* tab = reinterpret_cast<unsigned*>(smem + C::QS);
+    unsigned* tab = reinterpret_cast<unsigned*>(smem + QS);
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m16 = lane & 15, q4 = lane >> 4;
     const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
@@ -245,12 +313,26 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
     const int k0 = tile * kSnapColKeys;
     if (k0 >= n) return;
     const int k1 = min(k0 + kSnapColKeys, n);
-    const int NT = (a.R + 15) / 16;
+    const int bs = a.bs, sh = (bs & (bs - 1)) == 0 ? __builtin_ctz(bs) : -1;
+    const int blk0 = div_bs(k0, bs, sh);
     if (tid == 0) s_bad = 0;
+    __syncthreads();
+    if (stage_blocks(a, b, g, k0, k1, tab)) s_bad = 1;
+    __syncthreads();
+
+    // The first two chunks are in flight while the queries and row constants are staged.
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k);
+    constexpr int stride = kW * 32;
+    uint4 kA[2][KS], kB[2][KS];
+    unsigned okA[2], okB[2];
+    int c = k0 + wid * 32;
+    load_k<D>(kp, tab, bs, sh, blk0, c, k1, m16, q4, kA, okA);
+    load_k<D>(kp, tab, bs, sh, blk0, c + stride, k1, m16, q4, kB, okB);
+
     // A operand of S = Q . K^T: lane supplies row m16 of the tile and dims q4*8.. of k-step ks,
     // which is exactly the operand-order staging used for the B operand of pass 1.
     stage_queries<D>(a, b, g, NT, qs);
-    for (int r = tid; r < NTMAX * 16; r += kW * 64) {
+    for (int r = tid; r < NT * 16; r += kW * 64) {
         float cr = __builtin_huge_valf();          // rows past R (or with no keys) add nothing
         if (r < a.R) {
             const float* pp = a.part1 + (((size_t)b * a.Hkv + g) * a.R + r) * a.nsplit1 * 2;
@@ -263,37 +345,36 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
                     if (pp[2 * s] != kNegInf) lam += __builtin_amdgcn_exp2f(pp[2 * s] - M) * pp[2 * s + 1];
             cr = nan ? __builtin_nanf("") : (lam > 0.f ? M + __log2f(lam) : __builtin_huge_valf());
         }
-        rowc[r] = cr;
+        rowc[r] = -cr;                                     // negated: the exponent is one fma
     }
-    if (stage_blocks(a, b, g, k0, k1, tab)) s_bad = 1;
     __syncthreads();
 
-    const int blk0 = k0 / a.bs;
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     float* dst = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
     const bool poisoned = s_bad != 0;
+    const float sc = fabsf(a.scale_log2);
 
-    auto consume = [&](int c0, uint4 (&kr)[2][KS], unsigned (&okm)[2]) {
+    auto consume = [&](int c0, const uint4 (&kr)[2][KS], const unsigned (&okm)[2]) {
         float col[2] = {0.f, 0.f};
+        uint4 qv[2][KS];
+        f32x4 acc[2][2];
+        read_q<KS>(qs, 0, lane, qv[0]);
+        read_q<KS>(qs, 1, lane, qv[1]);
+        score_tile<KS, true>(qv[0], kr, acc[0]);
 #pragma unroll
-        for (int t = 0; t < NTMAX; ++t) {
-            if (t >= NT) break;
-            uint4 qa[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qa[ks] = qs[(t * KS + ks) * 64 + lane];
-            const float4 rc = *reinterpret_cast<const float4*>(&rowc[t * 16 + q4 * 4]);
+        for (int t = 0; t < NT; ++t) {
+            if (t + 1 < NT) score_tile<KS, true>(qv[(t + 1) & 1], kr, acc[(t + 1) & 1]);
+            if (t + 2 < NT) read_q<KS>(qs, t + 2, lane, qv[t & 1]);
+            const f32x4* cur = acc[t & 1];
+            const float4 rc = *reinterpret_cast<const float4*>(&rowc[t * 16 + q4 * 4]);   // -row constant
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(qa[ks]),
-                                                                 to_bf16x8(kr[kt][ks]), acc, 0, 0, 0);
-                col[kt] += __builtin_amdgcn_exp2f(acc[0] * a.scale_log2 - rc.x) +
-                           __builtin_amdgcn_exp2f(acc[1] * a.scale_log2 - rc.y) +
-                           __builtin_amdgcn_exp2f(acc[2] * a.scale_log2 - rc.z) +
-                           __builtin_amdgcn_exp2f(acc[3] * a.scale_log2 - rc.w);
+                const f32x4& s = cur[kt];
+                col[kt] += __builtin_amdgcn_exp2f(fmaf(s[0], sc, rc.x)) +
+                           __builtin_amdgcn_exp2f(fmaf(s[1], sc, rc.y)) +
+                           __builtin_amdgcn_exp2f(fmaf(s[2], sc, rc.z)) +
+                           __builtin_amdgcn_exp2f(fmaf(s[3], sc, rc.w));
             }
+            __builtin_amdgcn_sched_barrier(0);      // keep the per-tile issue order
         }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -307,36 +388,45 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
         }
     };
 
-    constexpr int stride = kW * 32;
-    uint4 kA[2][KS], kB[2][KS];
-    unsigned okA[2], okB[2];
-    int c = k0 + wid * 32;
-    load_k<D>(kp, tab, a.bs, blk0, c, k1, m16, q4, kA, okA);
     for (; c < k1; c += 2 * stride) {
-        load_k<D>(kp, tab, a.bs, blk0, c + stride, k1, m16, q4, kB, okB);
         consume(c, kA, okA);
+        load_k<D>(kp, tab, bs, sh, blk0, c + 2 * stride, k1, m16, q4, kA, okA);
         if (c + stride >= k1) break;
-        load_k<D>(kp, tab, a.bs, blk0, c + 2 * stride, k1, m16, q4, kA, okA);
         consume(c + stride, kB, okB);
+        load_k<D>(kp, tab, bs, sh, blk0, c + 3 * stride, k1, m16, q4, kB, okB);
     }
 }
 
-template <int D, int NTMAX>
+template <int D, int NT>
 hipError_t launch_passes(const SnapArgs& a, hipStream_t s) {
-    snap_rowstats_mfma<D, NTMAX><<<dim3(a.nsplit1, a.Hkv, a.B), kW * 64, 0, s>>>(a);
+    snap_rowstats_mfma<D, NT><<<dim3(a.nsplit1, a.Hkv, a.B), kW * 64, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_stride == 0) return e;
     const dim3 grid((a.n_stride + kSnapColKeys - 1) / kSnapColKeys, a.Hkv, a.B);
-    snap_colscore_mfma<D, NTMAX><<<grid, kW * 64, 0, s>>>(a);
+    snap_colscore_mfma<D, NT><<<grid, kW * 64, 0, s>>>(a);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const SnapArgs& a, hipStream_t s) {
+    // Row tiles rounded up to an even count (R <= 256 rows: at most 16 tiles).
+    switch ((((a.R + 15) / 16) + 1) / 2) {
+        case 1: return launch_passes<D, 2>(a, s);
+        case 2: return launch_passes<D, 4>(a, s);
+        case 3: return launch_passes<D, 6>(a, s);
+        case 4: return launch_passes<D, 8>(a, s);
+        case 5: return launch_passes<D, 10>(a, s);
+        case 6: return launch_passes<D, 12>(a, s);
+        case 7: return launch_passes<D, 14>(a, s);
+        case 8: return launch_passes<D, 16>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_snapkv_mfma_passes(const SnapArgs& a, hipStream_t s) {
-    const bool small = a.R <= 128;
-    if (a.D == 128) return small ? launch_passes<128, 8>(a, s) : launch_passes<128, 16>(a, s);
-    return small ? launch_passes<64, 8>(a, s) : launch_passes<64, 16>(a, s);
+    return a.D == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 
 }  // namespace kvss
