@@ -14,7 +14,8 @@ the reading taken is stated in the docstring.
 
 Modules
 -------
-kvcache    exact widening of stored values; paged-cache row gather
+kvcache    exact widening of stored values; paged-cache row gather, KV append, compact
+           draft rows
 attention  verify (gamma+1 causal queries), decode, sparse draft attention
 streaming  StreamingLLM sink + recent-window draft set
 snapkv     observation-window scoring, max-pool, per-KV-head top-k

@@ -41,3 +41,64 @@ def gather_rows(cache, block_table, b, g, positions):
 def gather_prefix(cache, block_table, b, g, length):
     """Rows [0, length) of sequence b, KV head g, as float64 [length, head_dim]."""
     return gather_rows(cache, block_table, b, g, np.arange(int(length)))
+
+
+def append_rows(k_cache, v_cache, block_table, k_new, v_new, start):
+    """Write T new K/V rows per sequence into copies of the paged caches.
+
+    MagicDec Section 3.1: the target scores gamma + 1 tokens per verify pass, and those
+    tokens' keys and values become part of the cache the pass attends to; Appendix A.1
+    (Fig. 8): the draft keeps its own compressed cache that grows the same way. The paper
+    prints no append rule; the reading taken: row t of sequence b goes to logical position
+    start[b] + t through the block table. A row whose position lies outside the table
+    (negative, or >= max_blocks * block_size) or whose physical block id is outside
+    [0, num_blocks) is not written.
+
+    k_new, v_new: [B, num_kv_heads, T, head_dim] in the caches' stored dtype. Returns
+    (k_cache', v_cache').
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    table = np.asarray(block_table)
+    nb, hkv, bs, _ = k_out.shape
+    B, H, T, _ = np.asarray(k_new).shape
+    for b in range(B):
+        for t in range(T):
+            pos = int(start[b]) + t
+            if pos < 0 or pos >= table.shape[1] * bs:
+                continue
+            blk = int(table[b, pos // bs])
+            if not 0 <= blk < nb:
+                continue
+            for g in range(H):
+                k_out[blk, g, pos % bs] = k_new[b, g, t]
+                v_out[blk, g, pos % bs] = v_new[b, g, t]
+    return k_out, v_out
+
+
+def compact_rows(cache, block_table, kv_lens, sel_idx, sel_count, tail_lo):
+    """The draft set of every (sequence, KV head) as one contiguous logical row list.
+
+    MagicDec Appendix A.1 (Fig. 8): the static compressed KV is generated at prefill and the
+    draft reads it. Reading: the compressed cache of (b, g) holds, in this order, the listed
+    rows sel_idx[b, g, 0:sel_count[b]] and then the recent rows [tail_lo[b], kv_lens[b]), so
+    a plain decode over it attends to exactly the draft set of draft_attention.
+
+    Returns a list over b of arrays [num_kv_heads, n_b, head_dim] in the stored dtype (rows
+    are copied, not widened) and the lengths n_b.
+    """
+    table = np.asarray(block_table)
+    bs = cache.shape[2]
+    out, lens = [], []
+    for b in range(len(kv_lens)):
+        L = int(kv_lens[b])
+        lo = min(max(int(tail_lo[b]), 0), L)
+        n = int(sel_count[b])
+        rows = []
+        for g in range(cache.shape[1]):
+            pos = np.concatenate([np.asarray(sel_idx[b, g, :n], dtype=np.int64),
+                                  np.arange(lo, L, dtype=np.int64)])
+            rows.append(cache[table[b, pos // bs], g, pos % bs, :])
+        out.append(np.stack(rows) if rows else np.zeros((0, 0, cache.shape[3]), cache.dtype))
+        lens.append(n + (L - lo))
+    return out, np.asarray(lens, dtype=np.int64)
