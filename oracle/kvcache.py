@@ -76,29 +76,51 @@ def append_rows(k_cache, v_cache, block_table, k_new, v_new, start):
     return k_out, v_out
 
 
-def compact_rows(cache, block_table, kv_lens, sel_idx, sel_count, tail_lo):
+def _nan_row(dtype, width):
+    """A row of NaN in the stored dtype (bf16 bit pattern 0x7FC0 for uint16 storage)."""
+    if np.dtype(dtype) == np.uint16:
+        return np.full(width, 0x7FC0, dtype=np.uint16)
+    return np.full(width, np.nan, dtype=dtype)
+
+
+def compact_rows(cache, block_table, kv_lens, sel_idx, sel_count, tail_lo, max_tail=None):
     """The draft set of every (sequence, KV head) as one contiguous logical row list.
 
     MagicDec Appendix A.1 (Fig. 8): the static compressed KV is generated at prefill and the
     draft reads it. Reading: the compressed cache of (b, g) holds, in this order, the listed
-    rows sel_idx[b, g, 0:sel_count[b]] and then the recent rows [tail_lo[b], kv_lens[b]), so
-    a plain decode over it attends to exactly the draft set of draft_attention.
+    rows sel_idx[b, g, 0:n] (n = sel_count[b] clamped to [0, k_max]) and then the recent rows
+    [tail_lo[b], kv_lens[b]), so a plain decode over it attends to exactly the draft set of
+    draft_attention. A compressed cache holds one row per slot, so a listed position outside
+    [0, tail_lo) (which the sparse draft would skip) cannot be left out; its slot holds a row
+    of NaN, as does every slot of a sequence whose tail is longer than max_tail (its length
+    is then cut to n + max_tail), so such inputs cannot pass unnoticed.
 
     Returns a list over b of arrays [num_kv_heads, n_b, head_dim] in the stored dtype (rows
     are copied, not widened) and the lengths n_b.
     """
     table = np.asarray(block_table)
-    bs = cache.shape[2]
+    nb, hkv, bs, D = cache.shape
+    k_max = sel_idx.shape[2]
     out, lens = [], []
     for b in range(len(kv_lens)):
         L = int(kv_lens[b])
         lo = min(max(int(tail_lo[b]), 0), L)
-        n = int(sel_count[b])
-        rows = []
-        for g in range(cache.shape[1]):
+        n = min(max(int(sel_count[b]), 0), k_max)
+        tail = L - lo
+        poison = max_tail is not None and tail > max_tail
+        if poison:
+            tail = max_tail
+        rows = np.empty((hkv, n + tail, D), dtype=cache.dtype)
+        for g in range(hkv):
             pos = np.concatenate([np.asarray(sel_idx[b, g, :n], dtype=np.int64),
-                                  np.arange(lo, L, dtype=np.int64)])
-            rows.append(cache[table[b, pos // bs], g, pos % bs, :])
-        out.append(np.stack(rows) if rows else np.zeros((0, 0, cache.shape[3]), cache.dtype))
-        lens.append(n + (L - lo))
+                                  np.arange(lo, lo + tail, dtype=np.int64)])
+            for j, p in enumerate(pos):
+                valid = (0 <= p < lo) if j < n else True
+                blk = int(table[b, p // bs]) if valid else -1
+                if poison or not valid or not 0 <= blk < nb:
+                    rows[g, j] = _nan_row(cache.dtype, D)
+                else:
+                    rows[g, j] = cache[blk, g, p % bs]
+        out.append(rows)
+        lens.append(n + tail)
     return out, np.asarray(lens, dtype=np.int64)

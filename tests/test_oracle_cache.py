@@ -139,3 +139,23 @@ def test_compact_rows_copy_stored_bits():
     for g in range(Hkv):
         for j, p in enumerate(expect_pos[g]):
             np.testing.assert_array_equal(rows[0][g, j], k[table[0, p // bs], g, p % bs])
+
+
+def test_compact_rows_poison_invalid_inputs():
+    """Listed positions outside [0, tail_lo), bad block ids and over-long tails give NaN rows."""
+    rng = np.random.default_rng(31)
+    B, Hkv, mb, bs, D = 2, 1, 4, 4, 4
+    k = rng.standard_normal((B * mb, Hkv, bs, D)).astype(np.float32)
+    table = np.arange(B * mb, dtype=np.int32).reshape(B, mb)
+    table[1, 0] = 99                                       # rows 0..3 of sequence 1 unreadable
+    sel = np.array([[[2, 12, -1]], [[1, 5, 6]]], dtype=np.int32)
+    rows, lens = compact_rows(k, table, np.array([14, 10]), sel, np.array([2, 5]),
+                              np.array([10, 8]), max_tail=4)
+    np.testing.assert_array_equal(lens, [2 + 4, 3 + 2])    # sel_count clamps to k_max = 3
+    assert not np.isnan(rows[0][0, 0]).any()               # position 2: fine
+    assert np.isnan(rows[0][0, 1]).all()                   # 12 >= tail_lo: poisoned
+    assert np.isnan(rows[1][0, 0]).all()                   # block id 99
+    assert not np.isnan(rows[1][0, 1:]).any()
+    rows, lens = compact_rows(k, table, np.array([14, 10]), sel, np.array([2, 0]),
+                              np.array([10, 2]), max_tail=3)
+    assert lens[1] == 3 and np.isnan(rows[1]).all()       # tail 8 > max_tail 3
