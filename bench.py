@@ -33,13 +33,15 @@ COPY_BYTES = 1 << 30          # plain copy used to calibrate the HBM byte counte
 
 
 def source_digest():
-    """Digest of what decides the verify kernel's code: its source, the headers it includes and
-    the compiler flags."""
+    """Digest of what decides the verify kernel's code and launch: its source, the headers it
+    includes, the entry point that plans it, and the compiler flags."""
     import hashlib
     from kv_sparse_speculative_amd import build as kbuild
     h = hashlib.sha256()
-    for path in (KERNEL_SOURCE, os.path.join(os.path.dirname(KERNEL_SOURCE), "common.h"),
-                 os.path.join(os.path.dirname(KERNEL_SOURCE), "launch.h")):
+    csrc = os.path.dirname(KERNEL_SOURCE)
+    # the kernel, the headers it includes, and the entry point that plans its launch
+    for path in (KERNEL_SOURCE, os.path.join(csrc, "common.h"), os.path.join(csrc, "launch.h"),
+                 os.path.join(csrc, "api.hip")):
         h.update(open(path, "rb").read())
     h.update(" ".join(kbuild.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
@@ -156,6 +158,84 @@ def algorithmic_bytes(wl, P, T, sink, window, V):
     out["snapkv_select"] = int(P.sum()) * Hkv * D * eb + B * Hq * w * D * eb + B * Hkv * k * 4
     out["streaming_set"] = B * Hkv * sink * 4 + B * 12
     out["spec_accept"] = B * (2 * (T - 1) + 1) * V * 4 + B * T * 4
+    return out
+
+
+def measure_cache_maintenance(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
+    """The cache-maintenance calls around the hot path, each timed alone after a scrub read of
+    the K cache (so the last-level cache holds none of its bytes):
+      kv_append           the gamma + 1 verify rows of every sequence (rewritten in place with
+                          the values already stored, so the cache is unchanged)
+      draft_cache_build   the compact SnapKV draft cache, built once per prompt
+      draft_snapkv_compact one draft step as a plain T = 1 decode over the compact cache,
+                          next to the gathered SnapKV draft it replaces."""
+    import numpy as np
+    import torch
+    from kv_sparse_speculative_amd import kvss
+
+    dev = ns.k_cache.device
+    B, Hkv, D, T = ns.batch, wl.num_kv_heads, wl.head_dim, ns.T
+    eb = ns.k_cache.element_size()
+    P = ns.prompt_lens_np
+    budget, w, _ = wl.snapkv
+    k = budget - w
+    stream = torch.cuda.current_stream()
+    sink_buf = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # the verify rows as they are stored (positions P .. P + T - 1)
+    pos = torch.from_numpy(P.astype(np.int64))[:, None] + torch.arange(T)[None, :]
+    bs = wl.block_size
+    blk = torch.gather(ns.block_table.cpu().long(), 1, pos // bs)
+    k_new = ns.k_cache[blk.to(dev), :, (pos % bs).to(dev)].permute(0, 2, 1, 3).contiguous()
+    v_new = ns.v_cache[blk.to(dev), :, (pos % bs).to(dev)].permute(0, 2, 1, 3).contiguous()
+    start = ns.prompt_lens.clone()
+
+    cap = k + w + 1
+    cb = (cap + bs - 1) // bs
+    ck = torch.empty((B * cb, Hkv, bs, D), dtype=ns.k_cache.dtype, device=dev)
+    cv = torch.empty_like(ck)
+    ctab = torch.arange(B * cb, dtype=torch.int32, device=dev).view(B, cb)
+    clens = torch.empty(B, dtype=torch.int32, device=dev)
+    kv_c = kvss.PagedKV(ck, cv, ctab, clens, cap)
+    q1 = ns.q_draft.unsqueeze(2).contiguous()
+    o1 = torch.empty((B, wl.num_q_heads, 1, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    calls = {
+        "kv_append": lambda: kvss.kvss_kv_append(kv_p, k_new, v_new, start),
+        "draft_cache_build": lambda: kvss.kvss_draft_cache_build(kv_d, sel, cnt, tail, w + 1, kv_c,
+                                                                 dst_lens=clens),
+        "draft_snapkv_compact": lambda: kvss.verify_attn_full(kv_c, q1, out=o1, want_lse=False,
+                                                              workspace=ws),
+    }
+    calls["draft_cache_build"]()
+    torch.cuda.synchronize()
+    n_rows = int(clens.sum().item())
+    row = Hkv * D * 2 * eb
+    q_out = B * wl.num_q_heads * D * (eb + 4)
+    nbytes = {"kv_append": 2 * B * T * row,
+              "draft_cache_build": 2 * n_rows * row + B * Hkv * k * 4,
+              "draft_snapkv_compact": n_rows * row + q_out}
+    out = {}
+    for name, fn in calls.items():
+        times = []
+        for _ in range(max(reps, 3) + 1):
+            kvss.kvss_stream_read(ns.k_cache, sink_buf)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times = sorted(times[1:])
+        ms = times[len(times) // 2]
+        gbs = nbytes[name] / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GB_per_s": round(gbs, 1),
+                     "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes[name]}
+    out["draft_snapkv_compact"]["tokens_per_s"] = round(B / (out["draft_snapkv_compact"]["ms"] * 1e-3), 1)
+    out["draft_snapkv_compact"]["speedup_vs_gather"] = round(
+        gather_detail["ms"] / out["draft_snapkv_compact"]["ms"], 3)
     return out
 
 
@@ -351,6 +431,24 @@ def main():
     stream_gbs = ns.k_cache.numel() * ns.k_cache.element_size() / (rd[2] * 1e-3) / 1e9
 
     nbytes = algorithmic_bytes(wl, P, T, sink, window, ns.vocab)
+    # The same read at a draft call's size (one launch over as many bytes as the StreamingLLM
+    # draft moves, from rows no earlier read left in the last-level cache): the ceiling for a
+    # launch that short, ramp-up and drain included.
+    small = min(nbytes["draft_streaming"], ns.v_cache.numel() * ns.v_cache.element_size())
+    v_bytes = ns.v_cache.view(-1).view(torch.uint8)[:small]
+    rd = []
+    for _ in range(5):
+        kvss.kvss_stream_read(ns.k_cache, sink_buf)       # evicts the region read below
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kvss.kvss_stream_read(v_bytes, sink_buf)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rd.append(e0.elapsed_time(e1))
+    rd.sort()
+    small_gbs = small / (rd[2] * 1e-3) / 1e9
+
     total_bytes = sum(nbytes.values())
     detail = {}
     for c in calls:
@@ -362,6 +460,7 @@ def main():
             d["tokens_per_s"] = round(B * T / (ms * 1e-3), 1)
         if c.startswith("draft"):
             d["tokens_per_s"] = round(B / (ms * 1e-3), 1)
+            d["frac_stream_same_size"] = round(gbs / small_gbs, 4)
         detail[c] = d
     v = detail["verify"]
     result = {
@@ -385,7 +484,10 @@ def main():
                      "kernel": "verify_attn_full"},
         "calls": detail,
         "stream_read_GB_per_s": round(stream_gbs, 1),
+        "stream_read_draft_size": {"bytes": small, "GB_per_s": round(small_gbs, 1)},
     }
+    result["next"] = measure_cache_maintenance(wl, ns, kv_p, kv_d, sel, cnt, tail, args.steps,
+                                               detail["draft_snapkv"])
     if args.copy_reference:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

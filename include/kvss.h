@@ -14,6 +14,9 @@
  *   draft_attn_sparse  T_D      : one draft query per sequence over a sparse subset
  *   verify_attn_full   T_V      : gamma + 1 causal queries per sequence over the full cache
  *   spec_accept        Omega    : greedy / rejection-sampling acceptance
+ * and the cache maintenance around them (Section 3.1; Appendix A.1, Fig. 8):
+ *   kvss_kv_append          append the newly scored tokens' K/V rows to a paged cache
+ *   kvss_draft_cache_build  materialise the compressed draft cache once at prefill
  *
  * Conventions (all calls)
  *   - Every pointer argument that names a tensor is a DEVICE pointer owned by the caller; the
@@ -198,6 +201,54 @@ KVSS_API int spec_accept(const float* target_logits, const float* draft_logits,
                 const int32_t* draft_tokens, int batch, int gamma, int vocab, float temperature,
                 uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
                 float* row_stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvss_kv_append -- write T new K/V rows per sequence into a paged cache (MagicDec
+ * Section 3.1: the gamma + 1 tokens a verify pass scores are part of the cache it attends
+ * to; Appendix A.1, Fig. 8: the compressed draft cache grows the same way).
+ *   kv            the cache written; the call writes through kv->k and kv->v (kv_lens and
+ *                 max_kv_len are not used: the caller advances its lengths itself)
+ *   k_new, v_new  [batch, num_kv_heads, T, head_dim] of kv->dtype, 16-byte aligned
+ *   start         int32 [batch] (device): row t of sequence b goes to logical position
+ *                 start[b] + t, i.e. physical block block_table[b, pos / block_size] at
+ *                 offset pos % block_size.
+ * A row whose position is negative or >= max_blocks * block_size, or whose block id lies
+ * outside [0, num_blocks), is not written. Sequences must not share the blocks being
+ * written (concurrent writes to one row are not ordered). T == 0 or batch == 0: no-op.
+ */
+KVSS_API int kvss_kv_append(const kvss_kv* kv, const void* k_new, const void* v_new, int T,
+                            const int32_t* start, void* stream);
+
+/*
+ * kvss_draft_cache_build -- materialise the compressed draft cache once at prefill (MagicDec
+ * Appendix A.1, Fig. 8: the static compressed KV is generated during prefill and used for
+ * drafting). For every (sequence b, KV head g) the compact cache `dst` receives, as logical
+ * rows 0 .. n_b - 1:
+ *     src rows sel_idx[b, g, 0 : n] (n = sel_count[b] clamped to [0, k_max]), in list order,
+ *     then src rows [tail_lo[b], L_b), L_b = src->kv_lens[b] clamped to src->max_kv_len,
+ * and dst_lens[b] = n_b. A plain decode over dst (verify_attn_full with T = 1, kv_lens =
+ * dst_lens) then attends to exactly the set draft_attn_sparse reads from src.
+ *   src           the target cache (read only)
+ *   sel_idx       int32 [batch, num_kv_heads, k_max], ascending positions < tail_lo[b]
+ *                 (as snapkv_select or kvss_streaming_set produce); NULL allowed if k_max == 0
+ *   sel_count     int32 [batch]; NULL allowed if k_max == 0
+ *   tail_lo       int32 [batch]
+ *   max_tail      host bound on L_b - tail_lo[b]
+ *   dst           compact cache, same batch, num_kv_heads, head_dim and dtype as src, its own
+ *                 block table and storage (must not alias src); k_max + max_tail must not
+ *                 exceed dst->max_blocks * dst->block_size. dst->kv_lens and max_kv_len are
+ *                 not used.
+ *   dst_lens      int32 [batch] (device), written.
+ * A compact cache holds one row per slot, so inputs it cannot represent are made visible
+ * rather than dropped: a listed position outside [0, tail_lo[b]) or a src block id outside
+ * [0, src->num_blocks) gives a row of NaN, and a sequence whose tail exceeds max_tail gets
+ * NaN in every slot (its length is then n + max_tail). A dst block id outside
+ * [0, dst->num_blocks) is not written.
+ */
+KVSS_API int kvss_draft_cache_build(const kvss_kv* src, const int32_t* sel_idx,
+                                    const int32_t* sel_count, int k_max, const int32_t* tail_lo,
+                                    int max_tail, const kvss_kv* dst, int32_t* dst_lens,
+                                    void* stream);
 
 /*
  * kvss_stream_read -- measurement reference, not part of the method: reads `bytes` (rounded

@@ -48,6 +48,7 @@ constexpr long kSnapTargetWorkgroups = 3 * 256 * 4;
 constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes per round
 constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
 constexpr int kMaxGamma = 31;      // speculation length limit of spec_accept
+constexpr int kMaxGridYZ = 65535;  // batch and KV heads index the y / z grid dimensions
 
 struct Plan {
     int nsplit;
@@ -55,13 +56,14 @@ struct Plan {
 };
 
 // Split a virtual key range of up to max_total keys per (sequence, KV head) so that the
-// launch offers about kTargetWorkgroups workgroups, each doing at least four rounds.
+// launch offers about kTargetWorkgroups workgroups, each doing at least eight rounds (a
+// shorter split would not pay for the extra merge launch and partial traffic).
 Plan plan_splits(long pairs, long max_total, int unit, long max_len = 1L << 30,
                  long target = kTargetWorkgroups) {
     Plan p{1, unit};
     if (max_total <= 0 || pairs <= 0) return p;
     const long want = ceil_div(target, pairs);
-    const long useful = ceil_div(max_total, 4L * unit);
+    const long useful = ceil_div(max_total, 8L * unit);
     long ns = want < useful ? want : useful;
     if (ns < 1) ns = 1;
     if (ceil_div(max_total, ns) > max_len) ns = ceil_div(max_total, max_len);
@@ -82,6 +84,9 @@ int check_kv(const kvss_kv* kv) {
     if (kv->block_size <= 0 || kv->block_size % 16 != 0)
         return fail(KVSS_EUNSUPPORTED, "block_size %d is not a positive multiple of 16", kv->block_size);
     if (kv->num_kv_heads <= 0) return fail(KVSS_EINVAL, "num_kv_heads must be >= 1");
+    if (kv->batch > kMaxGridYZ || kv->num_kv_heads > kMaxGridYZ)
+        return fail(KVSS_EUNSUPPORTED, "batch %d or num_kv_heads %d exceeds %d", kv->batch,
+                    kv->num_kv_heads, kMaxGridYZ);
     if (kv->max_kv_len < 0) return fail(KVSS_EINVAL, "max_kv_len must be >= 0");
     if (kv->batch == 0) return ok();
     if (kv->max_blocks <= 0 || kv->num_blocks <= 0)
@@ -91,6 +96,8 @@ int check_kv(const kvss_kv* kv) {
                     (long)kv->max_blocks * kv->block_size);
     if (!kv->k || !kv->v || !kv->block_table || !kv->kv_lens)
         return fail(KVSS_EINVAL, "kv tensors (k, v, block_table, kv_lens) must be non-NULL");
+    if ((long long)kv->num_blocks * kv->num_kv_heads * kv->block_size > 0xffffffffLL)
+        return fail(KVSS_EUNSUPPORTED, "cache rows num_blocks * num_kv_heads * block_size exceed 2^32 - 1");
     return ok();
 }
 
@@ -167,6 +174,8 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     s.total = s.part1 + s.scores + s.pooled;
     return s;
 }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -376,6 +385,85 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
     a.out_num = out_num_accepted;
     return hip_status(kvss::launch_accept(a, workspace, static_cast<hipStream_t>(stream)),
                       "accept launch");
+}
+
+int kvss_kv_append(const kvss_kv* kv, const void* k_new, const void* v_new, int T,
+                   const int32_t* start, void* stream) {
+    int rc = check_kv(kv);
+    if (rc) return rc;
+    if (T < 0) return fail(KVSS_EINVAL, "T must be >= 0 (got %d)", T);
+    if (kv->batch == 0 || T == 0) return ok();
+    if ((long long)kv->batch * T > 0x7fffffffLL)
+        return fail(KVSS_EUNSUPPORTED, "batch * T = %lld rows exceeds 2^31 - 1", (long long)kv->batch * T);
+    if (!k_new || !v_new || !start) return fail(KVSS_EINVAL, "k_new, v_new and start must be non-NULL");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kv->k) || !aligned16(kv->v))
+        return fail(KVSS_EINVAL, "k, v, k_new and v_new must be 16-byte aligned");
+    kvss::AppendArgs a{};
+    a.k = const_cast<void*>(kv->k);
+    a.v = const_cast<void*>(kv->v);
+    a.block_table = kv->block_table;
+    a.B = kv->batch;
+    a.Hkv = kv->num_kv_heads;
+    a.bs = kv->block_size;
+    a.max_blocks = kv->max_blocks;
+    a.num_blocks = kv->num_blocks;
+    a.row_bytes = kv->head_dim * (kv->dtype == KVSS_BF16 ? 2 : 4);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.T = T;
+    a.start = start;
+    return hip_status(kvss::launch_kv_append(a, static_cast<hipStream_t>(stream)), "kv append launch");
+}
+
+int kvss_draft_cache_build(const kvss_kv* src, const int32_t* sel_idx, const int32_t* sel_count,
+                           int k_max, const int32_t* tail_lo, int max_tail, const kvss_kv* dst,
+                           int32_t* dst_lens, void* stream) {
+    int rc = check_kv(src);
+    if (rc) return rc;
+    if ((rc = check_kv(dst))) return rc;
+    if (k_max < 0 || max_tail < 0)
+        return fail(KVSS_EINVAL, "k_max (%d) and max_tail (%d) must be >= 0", k_max, max_tail);
+    if (dst->batch != src->batch || dst->num_kv_heads != src->num_kv_heads ||
+        dst->head_dim != src->head_dim || dst->dtype != src->dtype)
+        return fail(KVSS_EINVAL, "dst must match src in batch, num_kv_heads, head_dim and dtype");
+    if (src->batch == 0) return ok();
+    if ((long long)k_max + max_tail > (long long)dst->max_blocks * dst->block_size)
+        return fail(KVSS_EINVAL, "k_max + max_tail = %lld exceeds the compact capacity %lld",
+                    (long long)k_max + max_tail, (long long)dst->max_blocks * dst->block_size);
+    if (k_max > 0 && (!sel_idx || !sel_count))
+        return fail(KVSS_EINVAL, "sel_idx and sel_count must be non-NULL when k_max > 0");
+    if (!tail_lo || !dst_lens) return fail(KVSS_EINVAL, "tail_lo and dst_lens must be non-NULL");
+    if (!aligned16(src->k) || !aligned16(src->v) || !aligned16(dst->k) || !aligned16(dst->v))
+        return fail(KVSS_EINVAL, "cache tensors must be 16-byte aligned");
+    if (src->k == dst->k || src->v == dst->v || src->k == dst->v || src->v == dst->k)
+        return fail(KVSS_EINVAL, "dst must not alias src");
+    kvss::CompactArgs a{};
+    a.k = src->k;
+    a.v = src->v;
+    a.block_table = src->block_table;
+    a.kv_lens = src->kv_lens;
+    a.B = src->batch;
+    a.Hkv = src->num_kv_heads;
+    a.bs = src->block_size;
+    a.max_blocks = src->max_blocks;
+    a.num_blocks = src->num_blocks;
+    a.max_kv_len = src->max_kv_len;
+    a.row_bytes = src->head_dim * (src->dtype == KVSS_BF16 ? 2 : 4);
+    a.dtype = src->dtype;
+    a.sel_idx = k_max > 0 ? sel_idx : nullptr;
+    a.sel_count = k_max > 0 ? sel_count : nullptr;
+    a.tail_lo = tail_lo;
+    a.k_max = k_max;
+    a.max_tail = max_tail;
+    a.dst_k = const_cast<void*>(dst->k);
+    a.dst_v = const_cast<void*>(dst->v);
+    a.dst_table = dst->block_table;
+    a.dst_bs = dst->block_size;
+    a.dst_max_blocks = dst->max_blocks;
+    a.dst_num_blocks = dst->num_blocks;
+    a.dst_lens = dst_lens;
+    return hip_status(kvss::launch_compact_build(a, static_cast<hipStream_t>(stream)),
+                      "draft cache build launch");
 }
 
 int kvss_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {

@@ -61,6 +61,40 @@ struct SnapArgs {
 hipError_t launch_snapkv(const SnapArgs& a, hipStream_t s);
 hipError_t launch_snapkv_mfma_passes(const SnapArgs& a, hipStream_t s);
 
+// Append T rows per sequence to a paged cache (k_new / v_new [B, Hkv, T, D]).
+struct AppendArgs {
+    void* k;
+    void* v;
+    const int32_t* block_table;
+    int B, Hkv, bs, max_blocks, num_blocks, row_bytes;
+    const void* k_new;
+    const void* v_new;
+    int T;
+    const int32_t* start;       // [B] logical position of row 0
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+
+// Copy each (sequence, KV head)'s draft set (listed rows, then the tail) into a compact cache.
+struct CompactArgs {
+    const void* k;
+    const void* v;
+    const int32_t* block_table;
+    const int32_t* kv_lens;
+    int B, Hkv, bs, max_blocks, num_blocks, max_kv_len, row_bytes, dtype;
+    const int32_t* sel_idx;     // [B, Hkv, k_max] or null when k_max == 0
+    const int32_t* sel_count;   // [B] or null when k_max == 0
+    const int32_t* tail_lo;     // [B]
+    int k_max, max_tail;
+    void* dst_k;
+    void* dst_v;
+    const int32_t* dst_table;   // [B, dst_max_blocks]
+    int dst_bs, dst_max_blocks, dst_num_blocks;
+    int32_t* dst_lens;          // [B]
+};
+
+hipError_t launch_compact_build(const CompactArgs& a, hipStream_t s);
+
 hipError_t launch_streaming_set(const int32_t* kv_lens, int B, int Hkv, int sink, int window,
                                 int32_t* sel_idx, int32_t* sel_count, int32_t* tail_lo,
                                 hipStream_t s);

@@ -57,6 +57,8 @@ _SIGNATURES = {
     "kvss_accept_workspace_bytes": (_Z, [_I, _I, _I]),
     "spec_accept": (_I, [_P, _P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _Z, _P]),
     "kvss_stream_read": (_I, [_P, _Z, _P, _P]),
+    "kvss_kv_append": (_I, [_KV, _P, _P, _I, _P, _P]),
+    "kvss_draft_cache_build": (_I, [_KV, _P, _P, _I, _P, _I, _KV, _P, _P]),
 }
 
 _lib = None
@@ -262,3 +264,34 @@ def kvss_stream_read(buf, sink, stream=None):
     _need(sink, "sink")
     _check(lib().kvss_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
                                   _stream(stream)))
+
+
+def kvss_kv_append(kv, k_new, v_new, start, stream=None):
+    """Write k_new / v_new [B, Hkv, T, D] at logical positions start[b] + t of the paged cache."""
+    _need(k_new, "k_new", kv.dtype)
+    _need(v_new, "v_new", kv.dtype)
+    _need(start, "start", torch.int32)
+    B, H, T, D = k_new.shape
+    if v_new.shape != k_new.shape or B != kv.batch or H != kv.num_kv_heads or D != kv.head_dim:
+        raise ValueError("k_new / v_new must be [batch, num_kv_heads, T, head_dim] of the cache")
+    _check(lib().kvss_kv_append(ctypes.byref(kv.desc()), k_new.data_ptr(), v_new.data_ptr(), T,
+                                start.data_ptr(), _stream(stream)))
+
+
+def kvss_draft_cache_build(src, sel_idx, sel_count, tail_lo, max_tail, dst, dst_lens=None,
+                           stream=None):
+    """Compact draft cache: dst receives each (b, g)'s listed rows then the tail of src;
+    returns dst_lens int32 [B]."""
+    k_max = 0 if sel_idx is None else sel_idx.shape[-1]
+    if sel_idx is not None:
+        _need(sel_idx, "sel_idx", torch.int32)
+        _need(sel_count, "sel_count", torch.int32)
+    _need(tail_lo, "tail_lo", torch.int32)
+    if dst_lens is None:
+        dst_lens = torch.empty(src.batch, dtype=torch.int32, device=tail_lo.device)
+    _need(dst_lens, "dst_lens", torch.int32)
+    _check(lib().kvss_draft_cache_build(ctypes.byref(src.desc()), _ptr(sel_idx), _ptr(sel_count),
+                                        k_max, tail_lo.data_ptr(), int(max_tail),
+                                        ctypes.byref(dst.desc()), dst_lens.data_ptr(),
+                                        _stream(stream)))
+    return dst_lens

@@ -45,6 +45,8 @@ def _verify(d, Hq=8, T=5, ws=None, wsb=0, q=FAKE, out=FAKE, scale=0.1):
     ("max_kv_len", 65, kvss.KVSS_EINVAL),       # > max_blocks * block_size
     ("k", None, kvss.KVSS_EINVAL),
     ("block_table", None, kvss.KVSS_EINVAL),
+    ("batch", 70000, kvss.KVSS_EUNSUPPORTED),   # indexes a grid dimension
+    ("num_blocks", 1 << 28, kvss.KVSS_EUNSUPPORTED),   # rows beyond 32-bit indexing
 ])
 def test_kv_descriptor_validation(field, value, code):
     assert _verify(_desc(**{field: value})) == code
@@ -110,3 +112,41 @@ def test_accept_and_streaming_validation():
     assert L.kvss_accept_workspace_bytes(4, 3, 100) >= 4 * 7 * 16
     assert L.kvss_streaming_set(FAKE, 2, 2, -1, 4, FAKE, FAKE, FAKE, None) == kvss.KVSS_EINVAL
     assert L.kvss_streaming_set(None, 2, 2, 4, 4, FAKE, FAKE, FAKE, None) == kvss.KVSS_EINVAL
+
+
+def test_append_validation():
+    lib = kvss.lib()
+    d = _desc()
+    app = lambda d, T=3, k=FAKE, v=FAKE, start=FAKE: lib.kvss_kv_append(ctypes.byref(d), k, v, T,
+                                                                         start, None)
+    assert app(d, T=-1) == kvss.KVSS_EINVAL
+    assert app(d, k=None) == kvss.KVSS_EINVAL
+    assert app(d, start=None) == kvss.KVSS_EINVAL
+    assert app(d, k=FAKE + 8) == kvss.KVSS_EINVAL            # not 16-byte aligned
+    assert app(_desc(dtype=5)) == kvss.KVSS_EUNSUPPORTED
+    assert app(d, T=0) == kvss.KVSS_OK                       # nothing to write: no launch
+    assert app(_desc(batch=0)) == kvss.KVSS_OK
+
+
+def test_draft_cache_build_validation():
+    lib = kvss.lib()
+    src = _desc()
+    dst = _desc(k=0x2000, v=0x3000, max_blocks=4, num_blocks=8, max_kv_len=0)
+
+    def build(src=src, dst=dst, sel=FAKE, cnt=FAKE, k_max=16, tail=FAKE, max_tail=32, lens=FAKE):
+        return lib.kvss_draft_cache_build(ctypes.byref(src), sel, cnt, k_max, tail, max_tail,
+                                          ctypes.byref(dst), lens, None)
+    assert build(k_max=-1) == kvss.KVSS_EINVAL
+    assert build(max_tail=-1) == kvss.KVSS_EINVAL
+    assert build(max_tail=64) == kvss.KVSS_EINVAL            # 16 + 64 > 4 * 16 slots
+    assert build(sel=None) == kvss.KVSS_EINVAL
+    assert build(cnt=None) == kvss.KVSS_EINVAL
+    assert build(tail=None) == kvss.KVSS_EINVAL
+    assert build(lens=None) == kvss.KVSS_EINVAL
+    assert build(dst=_desc(k=0x2000, v=0x3000, num_kv_heads=1)) == kvss.KVSS_EINVAL
+    assert build(dst=_desc(k=0x2000, v=0x3000, dtype=kvss.KVSS_F32)) == kvss.KVSS_EINVAL
+    assert build(dst=_desc(k=0x2000, v=0x3000, batch=3)) == kvss.KVSS_EINVAL
+    assert build(dst=_desc()) == kvss.KVSS_EINVAL            # aliases src
+    assert build(dst=_desc(k=0x2008, v=0x3000)) == kvss.KVSS_EINVAL   # misaligned
+    assert build(src=_desc(batch=0), dst=_desc(k=0x2000, v=0x3000, batch=0)) == kvss.KVSS_OK
+
