@@ -21,6 +21,7 @@ streaming  StreamingLLM sink + recent-window draft set
 snapkv     observation-window scoring, max-pool, per-KV-head top-k
 philox     Philox4x32-10 counter-based generator and the uniform mapping
 accept     greedy and rejection-sampling acceptance (Leviathan et al.)
+topk       dynamic Top-K draft attention (per-step selection)
 """
 
-from . import kvcache, attention, streaming, snapkv, philox, accept  # noqa: F401
+from . import kvcache, attention, streaming, snapkv, philox, accept, topk  # noqa: F401
