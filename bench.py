@@ -161,14 +161,16 @@ def algorithmic_bytes(wl, P, T, sink, window, V):
     return out
 
 
-def measure_cache_maintenance(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
-    """The cache-maintenance calls around the hot path, each timed alone after a scrub read of
-    the K cache (so the last-level cache holds none of its bytes):
-      kv_append           the gamma + 1 verify rows of every sequence (rewritten in place with
-                          the values already stored, so the cache is unchanged)
-      draft_cache_build   the compact SnapKV draft cache, built once per prompt
+def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
+    """The calls around the hot path, each timed alone after a scrub read of the K cache (so
+    the last-level cache holds none of its bytes):
+      kv_append            the gamma + 1 verify rows of every sequence (rewritten in place
+                           with the values already stored, so the cache is unchanged)
+      draft_cache_build    the compact SnapKV draft cache, built once per prompt
       draft_snapkv_compact one draft step as a plain T = 1 decode over the compact cache,
-                          next to the gathered SnapKV draft it replaces."""
+                           next to the gathered SnapKV draft it replaces
+      draft_topk_dynamic   one dynamic Top-K draft step (budget - 1 keys searched over the
+                           whole prefix, plus the current token), next to the static draft."""
     import numpy as np
     import torch
     from kv_sparse_speculative_amd import kvss
@@ -201,21 +203,32 @@ def measure_cache_maintenance(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_d
     o1 = torch.empty((B, wl.num_q_heads, 1, D), dtype=torch.float32, device=dev)
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
+    k_dyn = budget - 1
+    o_t = torch.empty((B, wl.num_q_heads, D), dtype=torch.float32, device=dev)
+    ws_t = torch.empty(max(kvss.lib().kvss_topk_workspace_bytes(
+        __import__("ctypes").byref(kv_d.desc()), wl.num_q_heads, k_dyn), 1), dtype=torch.uint8,
+        device=dev)
     calls = {
         "kv_append": lambda: kvss.kvss_kv_append(kv_p, k_new, v_new, start),
         "draft_cache_build": lambda: kvss.kvss_draft_cache_build(kv_d, sel, cnt, tail, w + 1, kv_c,
                                                                  dst_lens=clens),
         "draft_snapkv_compact": lambda: kvss.verify_attn_full(kv_c, q1, out=o1, want_lse=False,
                                                               workspace=ws),
+        "draft_topk_dynamic": lambda: kvss.draft_attn_topk(kv_d, ns.q_draft, k_dyn, out=o_t,
+                                                           want_lse=False, workspace=ws_t),
     }
     calls["draft_cache_build"]()
     torch.cuda.synchronize()
     n_rows = int(clens.sum().item())
     row = Hkv * D * 2 * eb
     q_out = B * wl.num_q_heads * D * (eb + 4)
+    L_d = P + 1
+    prefix_k = int((L_d - 1).sum()) * Hkv * D * eb                 # the search reads K once
+    dyn_rows = int(sum(min(k_dyn, int(x) - 1) + 1 for x in L_d))
     nbytes = {"kv_append": 2 * B * T * row,
               "draft_cache_build": 2 * n_rows * row + B * Hkv * k * 4,
-              "draft_snapkv_compact": n_rows * row + q_out}
+              "draft_snapkv_compact": n_rows * row + q_out,
+              "draft_topk_dynamic": prefix_k + dyn_rows * row + q_out}
     out = {}
     for name, fn in calls.items():
         times = []
@@ -236,6 +249,9 @@ def measure_cache_maintenance(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_d
     out["draft_snapkv_compact"]["tokens_per_s"] = round(B / (out["draft_snapkv_compact"]["ms"] * 1e-3), 1)
     out["draft_snapkv_compact"]["speedup_vs_gather"] = round(
         gather_detail["ms"] / out["draft_snapkv_compact"]["ms"], 3)
+    out["draft_topk_dynamic"]["tokens_per_s"] = round(B / (out["draft_topk_dynamic"]["ms"] * 1e-3), 1)
+    out["draft_topk_dynamic"]["cost_vs_static_draft"] = round(
+        out["draft_topk_dynamic"]["ms"] / gather_detail["ms"], 1)
     return out
 
 
@@ -486,7 +502,7 @@ def main():
         "stream_read_GB_per_s": round(stream_gbs, 1),
         "stream_read_draft_size": {"bytes": small, "GB_per_s": round(small_gbs, 1)},
     }
-    result["next"] = measure_cache_maintenance(wl, ns, kv_p, kv_d, sel, cnt, tail, args.steps,
+    result["next"] = measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, args.steps,
                                                detail["draft_snapkv"])
     if args.copy_reference:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)

@@ -12,6 +12,7 @@
  *   snapkv_select      T_select : static SnapKV selection at prefill (Section 4.4, App. A.1)
  *   kvss_streaming_set T_select : StreamingLLM sink + window set (Section 5.1, Table 1)
  *   draft_attn_sparse  T_D      : one draft query per sequence over a sparse subset
+ *   draft_attn_topk    T_select + T_D : the dynamic Top-K draft, subset searched every step
  *   verify_attn_full   T_V      : gamma + 1 causal queries per sequence over the full cache
  *   spec_accept        Omega    : greedy / rejection-sampling acceptance
  * and the cache maintenance around them (Section 3.1; Appendix A.1, Fig. 8):
@@ -201,6 +202,28 @@ KVSS_API int spec_accept(const float* target_logits, const float* draft_logits,
                 const int32_t* draft_tokens, int batch, int gamma, int vocab, float temperature,
                 uint64_t seed, uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
                 float* row_stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * draft_attn_topk -- dynamic Top-K draft attention (MagicDec Fig. 1(c): TopK attention has
+ * the highest acceptance of the drafts compared; Section 4.4, Static vs Dynamic: its subset is
+ * searched anew for every draft query, so the selection cost T_select(B, S, K) is paid on every
+ * draft step). One draft query per sequence (position kv_lens[b] - 1) attends to itself and to
+ * the k keys of [0, kv_lens[b] - 1) with the largest sum, over the G query heads of its KV head,
+ * of their softmax probabilities (for G = 1: the k largest raw scores); ties go to the lower
+ * position. This is snapkv_select with the query as a one-token window (w = 1, pool = 1,
+ * budget = k + 1) followed by draft_attn_sparse over that list and the tail [L - 1, L);
+ * both read the whole cache prefix, which is the dynamic selection's cost.
+ *   q         [batch, num_q_heads, head_dim] of kv->dtype
+ *   k         keys kept per (sequence, KV head), >= 1; sequences with fewer candidates keep all
+ *   out, lse  as for draft_attn_sparse (lse nullable)
+ *   sel_idx   nullable int32 [batch, num_kv_heads, k]: the kept positions, ascending, -1 pad
+ *   sel_count nullable int32 [batch]: kept count min(k, L - 1)
+ * Workspace: kvss_topk_workspace_bytes(kv, num_q_heads, k). Supported: G <= 32.
+ */
+KVSS_API size_t kvss_topk_workspace_bytes(const kvss_kv* kv, int num_q_heads, int k);
+KVSS_API int draft_attn_topk(const kvss_kv* kv, const void* q, int num_q_heads, int k, float scale,
+                             float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kvss_kv_append -- write T new K/V rows per sequence into a paged cache (MagicDec

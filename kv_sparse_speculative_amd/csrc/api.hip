@@ -466,6 +466,60 @@ int kvss_draft_cache_build(const kvss_kv* src, const int32_t* sel_idx, const int
                       "draft cache build launch");
 }
 
+// Dynamic Top-K draft: SnapKV-rule selection with the draft query as a one-token window,
+// then the gathered draft. Workspace = selection scratch | sel | count | tail_lo | draft.
+struct TopkLayout {
+    size_t snap, sel, cnt, tail, draft, total;
+};
+
+static TopkLayout topk_layout(const kvss_kv* kv, int num_q_heads, int k) {
+    TopkLayout t{};
+    t.snap = align_up(snap_layout(kv, num_q_heads, 1, true).total);
+    t.sel = align_up((size_t)kv->batch * kv->num_kv_heads * k * sizeof(int32_t));
+    t.cnt = align_up((size_t)kv->batch * sizeof(int32_t));
+    t.tail = t.cnt;
+    t.draft = align_up(partial_bytes((long)kv->batch * num_q_heads, draft_plan(kv, k, 1), kv->head_dim));
+    t.total = t.snap + t.sel + t.cnt + t.tail + t.draft;
+    return t;
+}
+
+size_t kvss_topk_workspace_bytes(const kvss_kv* kv, int num_q_heads, int k) {
+    if (check_kv(kv) != KVSS_OK || num_q_heads <= 0 || num_q_heads % kv->num_kv_heads || k <= 0)
+        return 0;
+    return topk_layout(kv, num_q_heads, k).total;
+}
+
+int draft_attn_topk(const kvss_kv* kv, const void* q, int num_q_heads, int k, float scale,
+                    float* out, float* lse, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int rc = check_kv(kv);
+    if (rc) return rc;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    const int G = num_q_heads / kv->num_kv_heads;
+    if (G > 32) return fail(KVSS_EUNSUPPORTED, "G = %d exceeds 32 query rows per KV head", G);
+    if (k <= 0) return fail(KVSS_EINVAL, "k must be >= 1 (got %d)", k);
+    if (!isfinite(scale)) return fail(KVSS_EINVAL, "scale must be finite");
+    if (kv->batch == 0) return ok();
+    if (!q || !out) return fail(KVSS_EINVAL, "q and out must be non-NULL");
+    const TopkLayout t = topk_layout(kv, num_q_heads, k);
+    if (workspace_bytes < t.total || !workspace)
+        return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, t.total);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* sel = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(ws + t.snap);
+    int32_t* cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(ws + t.snap + t.sel);
+    int32_t* tail = reinterpret_cast<int32_t*>(ws + t.snap + t.sel + t.cnt);
+    // The draft query [B, Hq, D] is the one-token observation window [B, Hq, 1, D].
+    if ((rc = snapkv_select(kv, q, num_q_heads, 1, 1, k + 1, scale, sel, cnt, nullptr, ws, t.snap,
+                            stream)))
+        return rc;
+    hipError_t e = kvss::launch_tail_lo(kv->kv_lens, kv->batch, kv->max_kv_len, 1, tail,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e, "tail launch");
+    return draft_attn_sparse(kv, q, num_q_heads, sel, cnt, k, tail, 1, scale, out, lse,
+                             ws + t.snap + t.sel + t.cnt + t.tail, t.draft, stream);
+}
+
 int kvss_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
     if (bytes == 0) return ok();
     if (!src || !sink) return fail(KVSS_EINVAL, "src and sink must be non-NULL");

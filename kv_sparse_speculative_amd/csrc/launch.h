@@ -95,6 +95,9 @@ struct CompactArgs {
 
 hipError_t launch_compact_build(const CompactArgs& a, hipStream_t s);
 
+hipError_t launch_tail_lo(const int32_t* kv_lens, int B, int max_kv_len, int back, int32_t* tail_lo,
+                          hipStream_t s);
+
 hipError_t launch_streaming_set(const int32_t* kv_lens, int B, int Hkv, int sink, int window,
                                 int32_t* sel_idx, int32_t* sel_count, int32_t* tail_lo,
                                 hipStream_t s);

@@ -25,7 +25,21 @@ __global__ __launch_bounds__(256) void streaming_set_kernel(const int32_t* kv_le
     }
 }
 
+// tail_lo[b] = max(min(kv_lens[b], max_kv_len) - back, 0): the start of the last `back` rows.
+__global__ __launch_bounds__(256) void tail_lo_kernel(const int32_t* kv_lens, int B, int max_kv_len,
+                                                      int back, int32_t* tail_lo) {
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b < B) tail_lo[b] = max(min(kv_lens[b], max_kv_len) - back, 0);
+}
+
 }  // namespace
+
+hipError_t launch_tail_lo(const int32_t* kv_lens, int B, int max_kv_len, int back, int32_t* tail_lo,
+                          hipStream_t s) {
+    if (B == 0) return hipSuccess;
+    tail_lo_kernel<<<(B + 255) / 256, 256, 0, s>>>(kv_lens, B, max_kv_len, back, tail_lo);
+    return hipGetLastError();
+}
 
 hipError_t launch_streaming_set(const int32_t* kv_lens, int B, int Hkv, int sink, int window,
                                 int32_t* sel_idx, int32_t* sel_count, int32_t* tail_lo,

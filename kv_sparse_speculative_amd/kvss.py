@@ -58,6 +58,8 @@ _SIGNATURES = {
     "spec_accept": (_I, [_P, _P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _Z, _P]),
     "kvss_stream_read": (_I, [_P, _Z, _P, _P]),
     "kvss_kv_append": (_I, [_KV, _P, _P, _I, _P, _P]),
+    "kvss_topk_workspace_bytes": (_Z, [_KV, _I, _I]),
+    "draft_attn_topk": (_I, [_KV, _P, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P]),
     "kvss_draft_cache_build": (_I, [_KV, _P, _P, _I, _P, _I, _KV, _P, _P]),
 }
 
@@ -295,3 +297,26 @@ def kvss_draft_cache_build(src, sel_idx, sel_count, tail_lo, max_tail, dst, dst_
                                         ctypes.byref(dst.desc()), dst_lens.data_ptr(),
                                         _stream(stream)))
     return dst_lens
+
+
+def draft_attn_topk(kv, q, k, scale=None, out=None, lse=None, want_lse=True, sel_idx=None,
+                    sel_count=None, workspace=None, stream=None):
+    """Dynamic Top-K draft: q [B, Hq, D] -> (out [B, Hq, D], lse [B, Hq] or None); the kept
+    positions go to sel_idx [B, Hkv, k] / sel_count [B] when given."""
+    _need(q, "q", kv.dtype)
+    B, Hq, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    for t, n in ((sel_idx, "sel_idx"), (sel_count, "sel_count")):
+        if t is not None:
+            _need(t, n, torch.int32)
+    d = kv.desc()
+    nbytes = lib().kvss_topk_workspace_bytes(ctypes.byref(d), Hq, int(k))
+    workspace, wsb = _workspace(nbytes, workspace, q.device)
+    _check(lib().draft_attn_topk(ctypes.byref(d), q.data_ptr(), Hq, int(k), scale, out.data_ptr(),
+                                 _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), wsb,
+                                 _stream(stream)))
+    return out, lse

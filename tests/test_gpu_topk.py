@@ -1,0 +1,86 @@
+"""GPU parity of the dynamic Top-K draft (draft_attn_topk) against the oracle: the attention
+output within the attention bound, the kept positions bit-exact against the same selection run
+through snapkv_select, and against the oracle's own set except at near-ties."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.snapkv as osnap
+from oracle.attention import decode_attention
+from oracle.topk import topk_draft_attention
+from kv_sparse_speculative_amd import kvss
+from kv_sparse_speculative_amd.synth import generate
+from kv_sparse_speculative_amd.workloads import WORKLOADS
+
+from _helpers import ATTN_RTOL, host, lse_err, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("tiny_fp32", {}, 48), ("llama8b_ctx8k", {"batch": 2}, 511),
+         ("qwen32b_ragged", {"batch": 3}, 1000), ("llama8b_ctx32k", {"batch": 1}, 511)]
+
+
+@pytest.mark.parametrize("name,kw,k", CASES, ids=[c[0] for c in CASES])
+def test_topk_draft_matches_oracle(name, kw, k):
+    torch.manual_seed(0)
+    ns = generate(WORKLOADS[name], device="cuda", parts=("attn",), **kw)
+    wl = ns.workload
+    L = ns.prompt_lens_np + 1
+    kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.kv_lens_draft, int(L.max()))
+    sel = torch.empty((ns.batch, wl.num_kv_heads, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(ns.batch, dtype=torch.int32, device="cuda")
+    out, lse = kvss.draft_attn_topk(kv, ns.q_draft, k, sel_idx=sel, sel_count=cnt)
+    # the same selection through the public SnapKV call, with its scores
+    q_obs = ns.q_draft.unsqueeze(2).contiguous()
+    s_sel, s_cnt, scores = kvss.snapkv_select(kv, q_obs, 1, 1, k + 1, want_scores=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(sel), host(s_sel))
+    np.testing.assert_array_equal(host(cnt), host(s_cnt))
+    # bit-exact: the oracle's top-k on the GPU's own scores
+    g_c = host(scores).astype(np.float64)
+    o_sel, o_cnt = osnap.select_from_scores(g_c, L, 1, 1, k + 1)
+    np.testing.assert_array_equal(host(sel), o_sel)
+    np.testing.assert_array_equal(host(cnt), o_cnt)
+
+    scale = 1 / math.sqrt(wl.head_dim)
+    ref, ref_lse, r_sel, r_cnt = topk_draft_attention(host(ns.q_draft), host(ns.k_cache),
+                                                      host(ns.v_cache), ns.block_table_np, L, k,
+                                                      scale)
+    np.testing.assert_array_equal(host(cnt), r_cnt)
+    flips = 0
+    ref_c = osnap.snapkv_scores(host(q_obs), host(ns.k_cache), ns.block_table_np, L, 1, scale)
+    for b in range(ns.batch):
+        n = int(L[b]) - 1
+        for g in range(wl.num_kv_heads):
+            a = set(host(sel)[b, g][host(sel)[b, g] >= 0].tolist())
+            r = set(r_sel[b, g][r_sel[b, g] >= 0].tolist())
+            diff = a ^ r
+            if diff:
+                tau = np.sort(ref_c[b, g, :n])[::-1][k - 1]
+                near = {j for j in diff if abs(ref_c[b, g, j] - tau) <= 1e-5 * tau}
+                assert diff == near, (b, g, sorted(diff - near)[:5])
+                flips += len(diff)
+    print(f"topk {name}: selection flips at near-ties {flips}")
+    if flips == 0:
+        err = row_rel_err(host(out), ref)
+        print(f"topk draft {name}: max row rel err {err:.3e}")
+        assert err <= ATTN_RTOL
+        assert lse_err(host(lse), ref_lse) <= 1e-4
+
+
+def test_topk_budget_covering_the_context_is_decode():
+    torch.manual_seed(0)
+    ns = generate(WORKLOADS["llama8b_ctx8k"], device="cuda", parts=("attn",), batch=3,
+                  prompt=(200, 900))
+    wl = ns.workload
+    L = ns.prompt_lens_np + 1
+    kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.kv_lens_draft, int(L.max()))
+    out, lse = kvss.draft_attn_topk(kv, ns.q_draft, int(L.max()))
+    torch.cuda.synchronize()
+    ref, ref_lse = decode_attention(host(ns.q_draft), host(ns.k_cache), host(ns.v_cache),
+                                    ns.block_table_np, L, 1 / math.sqrt(wl.head_dim))
+    assert row_rel_err(host(out), ref) <= ATTN_RTOL
+    assert lse_err(host(lse), ref_lse) <= 1e-4
