@@ -26,7 +26,7 @@ Outputs: out_tokens int32 [B, gamma + 1] (emitted tokens, then -1), num_accepted
 
 import numpy as np
 
-from .philox import accept_uniform, race_uniforms
+from .philox import accept_uniform, draft_uniforms, race_uniforms
 
 
 def softmax(z, temperature):
@@ -120,3 +120,26 @@ def spec_accept(target, draft, tokens, temperature, seed=0, offset=0, seq_ids=No
     if temperature == 0:
         return greedy_accept(target, tokens)
     return rejection_accept(target, draft, tokens, temperature, seed, offset, seq_ids)
+
+
+def draft_sample(logits, temperature, seed=0, offset=0, step=0, seq_ids=None):
+    """The draft token of one draft step from the draft's logits [B, V].
+
+    MagicDec Section 3.1: the draft proposes gamma tokens that the target then verifies with
+    the rule above; Section 5.1 drafts greedily. Reading: temperature 0 takes the argmax (ties
+    to the lowest id); temperature t > 0 draws from q = softmax(logits / t) by the same
+    exponential race as the emitted token, with the uniforms of oracle.philox.draft_uniforms
+    (a stream of its own, at position `step`). Returns int32 [B].
+    """
+    logits = np.asarray(logits)
+    B, V = logits.shape
+    ids = list(range(B)) if seq_ids is None else [int(x) for x in seq_ids]
+    out = np.empty(B, dtype=np.int32)
+    for b in range(B):
+        if temperature == 0:
+            out[b] = argmax_lowest(logits[b])
+        else:
+            out[b] = exponential_race(softmax(logits[b], temperature),
+                                      draft_uniforms(seed, offset, ids[b], step, V))
+    return out
+

@@ -15,7 +15,8 @@ reading taken here fixes a counter layout so that a decision can be replayed exa
   counter = (word block j, (stream << 16) | position, sequence b, offset & 0xffffffff)
 
 Stream 0 feeds the acceptance test of draft position i (word 0 of block 0); stream 1 feeds
-the exponential race at the emitting position (token x takes word x % 4 of block x // 4).
+the exponential race at the emitting position (token x takes word x % 4 of block x // 4);
+stream 2 feeds the race that samples the draft token of draft step i (same word layout).
 A 32-bit output x maps to the uniform u = (floor(x / 2^9) + 1/2) * 2^-23, which lies in
 (0, 1) and is exactly representable in binary32 and binary64 alike.
 """
@@ -30,6 +31,7 @@ MASK32 = 0xFFFFFFFF
 
 STREAM_ACCEPT = 0
 STREAM_RACE = 1
+STREAM_DRAFT = 2
 
 
 def philox4x32_10(counter, key):
@@ -70,12 +72,21 @@ def accept_uniform(seed, offset, b, position):
     return float(to_uniform(words[0]))
 
 
-def race_uniforms(seed, offset, b, position, vocab):
-    """Uniforms u'_x, x in [0, vocab), of the exponential race at `position` of sequence b."""
+def _race_words(stream, seed, offset, b, position, vocab):
     nblk = (int(vocab) + 3) // 4
     j = np.arange(nblk, dtype=np.uint64)
     ones = np.ones(nblk, dtype=np.uint64)
-    words = philox4x32_10((j, ones * ((STREAM_RACE << 16) | int(position)), ones * int(b),
+    words = philox4x32_10((j, ones * ((int(stream) << 16) | int(position)), ones * int(b),
                            ones * (int(offset) & MASK32)), _key(seed))
     u = np.stack([to_uniform(wd) for wd in words], axis=1).reshape(-1)
     return u[: int(vocab)]
+
+
+def race_uniforms(seed, offset, b, position, vocab):
+    """Uniforms u'_x, x in [0, vocab), of the exponential race at `position` of sequence b."""
+    return _race_words(STREAM_RACE, seed, offset, b, position, vocab)
+
+
+def draft_uniforms(seed, offset, b, step, vocab):
+    """Uniforms of the race that samples sequence b's draft token at draft step `step`."""
+    return _race_words(STREAM_DRAFT, seed, offset, b, step, vocab)

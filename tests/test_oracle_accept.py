@@ -15,9 +15,9 @@ import numpy as np
 import pytest
 from scipy import stats
 
-from oracle.accept import (argmax_lowest, exponential_race, greedy_accept, rejection_accept,
+from oracle.accept import (argmax_lowest, draft_sample, exponential_race, greedy_accept, rejection_accept,
                            rejection_accept_one, softmax)
-from oracle.philox import accept_uniform, philox4x32_10, race_uniforms, to_uniform
+from oracle.philox import accept_uniform, draft_uniforms, philox4x32_10, race_uniforms, to_uniform
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
 
@@ -156,3 +156,31 @@ def test_greedy_enumeration():
         assert n[0] == k
         assert list(out[0, :k + 1]) == list(xs[:k]) + [best[k]]
         assert np.all(out[0, k + 1:] == -1)
+
+
+def test_draft_sample_greedy_is_argmax():
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((6, 40))
+    logits[2, [5, 17]] = 10.0                     # a tie: the lower id wins
+    np.testing.assert_array_equal(draft_sample(logits, 0.0),
+                                  [int(np.flatnonzero(r == r.max())[0]) for r in logits])
+
+
+def test_draft_sample_law():
+    """Across offsets the sampled tokens follow softmax(logits / t) (chi-square)."""
+    z = np.array([[1.0, 0.2, -0.5, 2.0, 0.0, -1.5]])
+    t = 0.8
+    p = np.exp(z[0] / t - (z[0] / t).max())
+    p /= p.sum()
+    n = 20000
+    draws = np.array([draft_sample(z, t, seed=77, offset=o, step=2)[0] for o in range(n)])
+    counts = np.bincount(draws, minlength=z.shape[1])
+    assert stats.chisquare(counts, p * n).pvalue > 1e-3
+
+
+def test_draft_stream_is_independent_of_the_acceptance_race():
+    """Same (seed, offset, sequence, position): the draft and race streams draw different words."""
+    u_race = race_uniforms(5, 3, 1, 2, 64)
+    u_draft = draft_uniforms(5, 3, 1, 2, 64)
+    assert not np.any(u_race == u_draft)
+    assert abs(np.corrcoef(u_race, u_draft)[0, 1]) < 0.4
