@@ -170,7 +170,9 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
       draft_snapkv_compact one draft step as a plain T = 1 decode over the compact cache,
                            next to the gathered SnapKV draft it replaces
       draft_topk_dynamic   one dynamic Top-K draft step (budget - 1 keys searched over the
-                           whole prefix, plus the current token), next to the static draft."""
+                           whole prefix, plus the current token), next to the static draft
+      draft_sample         the draft token of one draft step from the draft's logits
+                           (temperature 1)."""
     import numpy as np
     import torch
     from kv_sparse_speculative_amd import kvss
@@ -203,6 +205,10 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
     o1 = torch.empty((B, wl.num_q_heads, 1, D), dtype=torch.float32, device=dev)
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
+    q_logits = ns.draft_logits[:, 0].contiguous()                     # the draft's logits [B, V]
+    d_tok = torch.empty(B, dtype=torch.int32, device=dev)
+    ws_s = torch.empty(kvss.lib().kvss_sample_workspace_bytes(B, q_logits.shape[1]),
+                       dtype=torch.uint8, device=dev)
     k_dyn = budget - 1
     o_t = torch.empty((B, wl.num_q_heads, D), dtype=torch.float32, device=dev)
     ws_t = torch.empty(max(kvss.lib().kvss_topk_workspace_bytes(
@@ -216,6 +222,8 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
                                                               workspace=ws),
         "draft_topk_dynamic": lambda: kvss.draft_attn_topk(kv_d, ns.q_draft, k_dyn, out=o_t,
                                                            want_lse=False, workspace=ws_t),
+        "draft_sample": lambda: kvss.draft_sample(q_logits, 1.0, seed=99, offset=1, step=0,
+                                                  tokens=d_tok, workspace=ws_s),
     }
     calls["draft_cache_build"]()
     torch.cuda.synchronize()
@@ -228,7 +236,8 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
     nbytes = {"kv_append": 2 * B * T * row,
               "draft_cache_build": 2 * n_rows * row + B * Hkv * k * 4,
               "draft_snapkv_compact": n_rows * row + q_out,
-              "draft_topk_dynamic": prefix_k + dyn_rows * row + q_out}
+              "draft_topk_dynamic": prefix_k + dyn_rows * row + q_out,
+              "draft_sample": q_logits.numel() * 4 + B * 4}
     out = {}
     for name, fn in calls.items():
         times = []

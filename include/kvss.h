@@ -15,6 +15,7 @@
  *   draft_attn_topk    T_select + T_D : the dynamic Top-K draft, subset searched every step
  *   verify_attn_full   T_V      : gamma + 1 causal queries per sequence over the full cache
  *   spec_accept        Omega    : greedy / rejection-sampling acceptance
+ *   draft_sample       the draft token of each draft step (greedy or sampled)
  * and the cache maintenance around them (Section 3.1; Appendix A.1, Fig. 8):
  *   kvss_kv_append          append the newly scored tokens' K/V rows to a paged cache
  *   kvss_draft_cache_build  materialise the compressed draft cache once at prefill
@@ -224,6 +225,25 @@ KVSS_API size_t kvss_topk_workspace_bytes(const kvss_kv* kv, int num_q_heads, in
 KVSS_API int draft_attn_topk(const kvss_kv* kv, const void* q, int num_q_heads, int k, float scale,
                              float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * draft_sample -- the draft token of one draft step (MagicDec Section 3.1: the draft proposes
+ * the gamma tokens the target verifies; Section 5.1 drafts greedily). From the draft's logits
+ * [batch, vocab] (fp32): temperature 0 takes the argmax (ties to the lowest id); temperature
+ * t > 0 draws from softmax(logits / t) by the exponential race spec_accept uses, on a Philox
+ * stream of its own (stream 2, position `step`, same key and offset conventions), so the draft
+ * token and the later acceptance draws are independent. The same statistics kernel as
+ * spec_accept's row statistics streams each row once.
+ *   step       draft step index within the round, in [0, 65535]
+ *   tokens     int32 [batch] (device), written
+ *   row_stats  nullable float [batch, 4]: max of z / t, sum of exp(z / t - max), 0, argmax
+ * Workspace: kvss_sample_workspace_bytes(batch, vocab). vocab < 2^24.
+ */
+KVSS_API size_t kvss_sample_workspace_bytes(int batch, int vocab);
+KVSS_API int draft_sample(const float* logits, int batch, int vocab, float temperature,
+                          uint64_t seed, uint64_t offset, int step, int32_t* tokens,
+                          float* row_stats, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * kvss_kv_append -- write T new K/V rows per sequence into a paged cache (MagicDec

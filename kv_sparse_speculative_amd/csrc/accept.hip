@@ -12,6 +12,8 @@
 //            over one slice of the emitting row, w = max(0, p - q) after a rejection (p if that
 //            is all zero) or p after full acceptance; re-reads only that row pair;
 //   finalize (sampling only) one wave per sequence: the winning token of the slices.
+// With gamma = 0 the same kernels sample one token per sequence from a single logit row (the
+// draft-token sampler): stats, an empty accept walk, and the race over that row.
 
 #include "common.h"
 #include "launch.h"
@@ -209,7 +211,8 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
     const int j0 = slice * per, j1 = min(nblk, j0 + per);
     RaceKey br{__builtin_huge_valf(), 0x7fffffff}, bp{__builtin_huge_valf(), 0x7fffffff};
     for (int j = j0 + tid; j < j1; j += kRaceThreads) {
-        uint32_t w0 = (uint32_t)j, w1 = (1u << 16) | (uint32_t)pos, w2 = (uint32_t)b, w3 = off;
+        uint32_t w0 = (uint32_t)j, w1 = ((uint32_t)a.race_stream << 16) | (uint32_t)(a.pos_base + pos),
+                 w2 = (uint32_t)b, w3 = off;
         philox4x32_10(w0, w1, w2, w3, k0, k1);
         const uint32_t w[4] = {w0, w1, w2, w3};
 #pragma unroll

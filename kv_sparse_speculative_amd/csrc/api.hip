@@ -2,6 +2,7 @@
 // workspace carving and error reporting. The operations are declared and specified in
 // include/kvss.h.
 
+#include <float.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -49,6 +50,8 @@ constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes
 constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
 constexpr int kMaxGamma = 31;      // speculation length limit of spec_accept
 constexpr int kMaxGridYZ = 65535;  // batch and KV heads index the y / z grid dimensions
+constexpr int kRaceStream = 1;     // Philox stream of the acceptance race
+constexpr int kDraftStream = 2;    // Philox stream of the draft-token race
 
 struct Plan {
     int nsplit;
@@ -173,6 +176,11 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     s.pooled = align_up(rows * s.n_stride * sizeof(float));
     s.total = s.part1 + s.scores + s.pooled;
     return s;
+}
+
+// 0 (greedy) or a finite positive temperature whose reciprocal is a finite float.
+bool temperature_ok(float t) {
+    return t == 0.f || (t > 0.f && isfinite(t) && 1.0 / (double)t < (double)FLT_MAX);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -359,8 +367,8 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
     if (gamma < 0) return fail(KVSS_EINVAL, "gamma must be >= 0");
     if (gamma > kMaxGamma) return fail(KVSS_EUNSUPPORTED, "gamma %d exceeds %d", gamma, kMaxGamma);
     if (vocab <= 0 || vocab >= (1 << 24)) return fail(KVSS_EINVAL, "vocab must be in [1, 2^24)");
-    if (!(temperature >= 0.f) || !isfinite(temperature))
-        return fail(KVSS_EINVAL, "temperature must be finite and >= 0");
+    if (!temperature_ok(temperature))
+        return fail(KVSS_EINVAL, "temperature must be finite and 0 or >= 1 / FLT_MAX");
     if (batch == 0) return ok();
     if (!target_logits || !out_tokens || !out_num_accepted || (gamma > 0 && !draft_tokens))
         return fail(KVSS_EINVAL, "target_logits, draft_tokens, out_tokens, out_num_accepted must be non-NULL");
@@ -383,8 +391,49 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
     a.stats = row_stats;
     a.out_tokens = out_tokens;
     a.out_num = out_num_accepted;
+    a.race_stream = kRaceStream;
+    a.pos_base = 0;
     return hip_status(kvss::launch_accept(a, workspace, static_cast<hipStream_t>(stream)),
                       "accept launch");
+}
+
+size_t kvss_sample_workspace_bytes(int batch, int vocab) {
+    if (batch < 0 || vocab <= 0) return 0;
+    return kvss_accept_workspace_bytes(batch, 0, vocab) + align_up((size_t)batch * sizeof(int32_t));
+}
+
+int draft_sample(const float* logits, int batch, int vocab, float temperature, uint64_t seed,
+                 uint64_t offset, int step, int32_t* tokens, float* row_stats, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    if (batch < 0) return fail(KVSS_EINVAL, "batch must be >= 0");
+    if (vocab <= 0 || vocab >= (1 << 24)) return fail(KVSS_EINVAL, "vocab must be in [1, 2^24)");
+    if (!temperature_ok(temperature))
+        return fail(KVSS_EINVAL, "temperature must be finite and 0 or >= 1 / FLT_MAX");
+    if (step < 0 || step > 0xffff) return fail(KVSS_EINVAL, "step must be in [0, 65535]");
+    if (batch == 0) return ok();
+    if (!logits || !tokens) return fail(KVSS_EINVAL, "logits and tokens must be non-NULL");
+    const size_t acc = kvss_accept_workspace_bytes(batch, 0, vocab);
+    const size_t need = kvss_sample_workspace_bytes(batch, vocab);
+    if (workspace_bytes < need || !workspace)
+        return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
+    // One logit row per sequence is the gamma = 0 acceptance problem: an empty accept walk
+    // and the race over that row, on the draft's own Philox stream at position `step`.
+    kvss::AcceptArgs a{};
+    a.target = logits;
+    a.B = batch;
+    a.gamma = 0;
+    a.V = vocab;
+    a.inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
+    a.seed = seed;
+    a.offset = offset;
+    a.stats = row_stats;
+    a.out_tokens = tokens;
+    a.out_num = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + acc);
+    a.race_stream = kDraftStream;
+    a.pos_base = step;
+    return hip_status(kvss::launch_accept(a, workspace, static_cast<hipStream_t>(stream)),
+                      "draft sample launch");
 }
 
 int kvss_kv_append(const kvss_kv* kv, const void* k_new, const void* v_new, int T,

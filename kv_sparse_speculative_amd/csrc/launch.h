@@ -112,6 +112,8 @@ struct AcceptArgs {
     float* stats;               // [B, 2*gamma+1, 4] or null
     int32_t* out_tokens;        // [B, gamma+1]
     int32_t* out_num;           // [B]
+    int race_stream;            // Philox stream of the exponential race
+    int pos_base;               // added to the emitting position in the race counter
 };
 
 // Workspace carve-up of one acceptance call: per-row slice partials, per-sequence decisions,

@@ -59,6 +59,8 @@ _SIGNATURES = {
     "kvss_stream_read": (_I, [_P, _Z, _P, _P]),
     "kvss_kv_append": (_I, [_KV, _P, _P, _I, _P, _P]),
     "kvss_topk_workspace_bytes": (_Z, [_KV, _I, _I]),
+    "kvss_sample_workspace_bytes": (_Z, [_I, _I]),
+    "draft_sample": (_I, [_P, _I, _I, _F, _U64, _U64, _I, _P, _P, _P, _Z, _P]),
     "draft_attn_topk": (_I, [_KV, _P, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P]),
     "kvss_draft_cache_build": (_I, [_KV, _P, _P, _I, _P, _I, _KV, _P, _P]),
 }
@@ -320,3 +322,22 @@ def draft_attn_topk(kv, q, k, scale=None, out=None, lse=None, want_lse=True, sel
                                  _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), wsb,
                                  _stream(stream)))
     return out, lse
+
+
+def draft_sample(logits, temperature, seed=0, offset=0, step=0, tokens=None, row_stats=None,
+                 want_stats=False, workspace=None, stream=None):
+    """Draft token per sequence from logits [B, V] f32 -> (tokens int32 [B], row_stats or None)."""
+    _need(logits, "logits", torch.float32)
+    B, V = logits.shape
+    dev = logits.device
+    if tokens is None:
+        tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    if row_stats is None and want_stats:
+        row_stats = torch.zeros((B, 4), dtype=torch.float32, device=dev)
+    nbytes = lib().kvss_sample_workspace_bytes(B, V)
+    workspace, wsb = _workspace(nbytes, workspace, dev)
+    _check(lib().draft_sample(logits.data_ptr(), B, V, float(temperature), int(seed) & (2**64 - 1),
+                              int(offset) & (2**64 - 1), int(step), tokens.data_ptr(),
+                              _ptr(row_stats), _ptr(workspace), wsb, _stream(stream)))
+    return tokens, row_stats
+

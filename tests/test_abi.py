@@ -150,3 +150,29 @@ def test_draft_cache_build_validation():
     assert build(dst=_desc(k=0x2008, v=0x3000)) == kvss.KVSS_EINVAL   # misaligned
     assert build(src=_desc(batch=0), dst=_desc(k=0x2000, v=0x3000, batch=0)) == kvss.KVSS_OK
 
+
+def test_draft_sample_and_topk_validation():
+    lib = kvss.lib()
+    smp = lambda B=2, V=10, t=1.0, step=0, logits=FAKE, tok=FAKE, ws=FAKE, wsb=1 << 20: lib.draft_sample(
+        logits, B, V, t, 1, 2, step, tok, None, ws, wsb, None)
+    assert smp(B=-1) == kvss.KVSS_EINVAL
+    assert smp(V=0) == kvss.KVSS_EINVAL
+    assert smp(V=1 << 24) == kvss.KVSS_EINVAL
+    assert smp(t=-1.0) == kvss.KVSS_EINVAL
+    assert smp(t=float("nan")) == kvss.KVSS_EINVAL
+    assert smp(t=1e-45) == kvss.KVSS_EINVAL                  # 1 / t overflows float
+    assert smp(step=1 << 16) == kvss.KVSS_EINVAL
+    assert smp(logits=None) == kvss.KVSS_EINVAL
+    assert smp(ws=None) == kvss.KVSS_EWORKSPACE
+    assert smp(wsb=8) == kvss.KVSS_EWORKSPACE
+    assert smp(B=0) == kvss.KVSS_OK
+    assert lib.kvss_sample_workspace_bytes(4, 1000) > 0
+    d = _desc()
+    topk = lambda d=d, Hq=8, k=16, ws=FAKE, wsb=1 << 30: lib.draft_attn_topk(
+        ctypes.byref(d), FAKE, Hq, k, 0.1, FAKE, None, None, None, ws, wsb, None)
+    assert topk(k=0) == kvss.KVSS_EINVAL
+    assert topk(Hq=7) == kvss.KVSS_EINVAL
+    assert topk(Hq=2 * 33) == kvss.KVSS_EUNSUPPORTED          # G = 33 > 32
+    assert topk(wsb=16) == kvss.KVSS_EWORKSPACE
+    assert lib.kvss_topk_workspace_bytes(ctypes.byref(d), 8, 16) > 0
+
