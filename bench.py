@@ -513,6 +513,11 @@ def main():
     }
     result["next"] = measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, args.steps,
                                                detail["draft_snapkv"])
+    if wl.name.startswith("llama8b"):
+        from kv_sparse_speculative_amd import speedup_model
+        rates = speedup_model.rates_from_bench(detail, result["next"], stream_gbs, B, maxP,
+                                               sink + window)
+        result["model"] = speedup_model.summary(rates, B, maxP)
     if args.copy_reference:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
