@@ -264,7 +264,7 @@ KVSS_API int kvss_kv_append(const kvss_kv* kv, const void* k_new, const void* v_
 
 /*
  * kvss_draft_cache_build -- materialise the compressed draft cache once at prefill (MagicDec
- * Appendix A.1, Fig. 8: the static compressed KV is generated during prefill and used for
+ * Appendix A.1, Fig. 8: the static compressed KV is built once at prefill and then read for
  * drafting). For every (sequence b, KV head g) the compact cache `dst` receives, as logical
  * rows 0 .. n_b - 1:
  *     src rows sel_idx[b, g, 0 : n] (n = sel_count[b] clamped to [0, k_max]), in list order,

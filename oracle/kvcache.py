@@ -86,7 +86,7 @@ def _nan_row(dtype, width):
 def compact_rows(cache, block_table, kv_lens, sel_idx, sel_count, tail_lo, max_tail=None):
     """The draft set of every (sequence, KV head) as one contiguous logical row list.
 
-    MagicDec Appendix A.1 (Fig. 8): the static compressed KV is generated at prefill and the
+    MagicDec Appendix A.1 (Fig. 8): the static compressed KV is built once at prefill and the
     draft reads it. Reading: the compressed cache of (b, g) holds, in this order, the listed
     rows sel_idx[b, g, 0:n] (n = sel_count[b] clamped to [0, k_max]) and then the recent rows
     [tail_lo[b], kv_lens[b]), so a plain decode over it attends to exactly the draft set of

@@ -1,7 +1,7 @@
 """Dynamic Top-K draft attention (oracle, test infrastructure).
 
 MagicDec names TopK attention as the dynamic selection with the highest acceptance rate
-(Fig. 1(c)) whose per-query search makes the selection cost "prohibitively high" (Section 4.4,
+(Fig. 1(c)) whose per-query search the paper judges too costly for selection (Section 4.4,
 Static vs Dynamic): unlike StreamingLLM or SnapKV, the subset is chosen anew for every draft
 query, so T_select(B, S, K) is paid on every draft step and grows with B * S. The paper gives
 no formula. Readings taken here:
