@@ -210,9 +210,28 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
     const int per = (nblk + nrace - 1) / nrace;
     const int j0 = slice * per, j1 = min(nblk, j0 + per);
     RaceKey br{__builtin_huge_valf(), 0x7fffffff}, bp{__builtin_huge_valf(), 0x7fffffff};
+    // rows are read as one 16-byte load per block of 4 tokens when they are 16-byte aligned
+    const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(zt) & 15) == 0 &&
+                     (!residual || (reinterpret_cast<uintptr_t>(zd) & 15) == 0);
     for (int j = j0 + tid; j < j1; j += kRaceThreads) {
         uint32_t w0 = (uint32_t)j, w1 = ((uint32_t)a.race_stream << 16) | (uint32_t)(a.pos_base + pos),
                  w2 = (uint32_t)b, w3 = off;
+        float vt[4], vd[4] = {0.f, 0.f, 0.f, 0.f};
+        if (vec) {
+            const float4 t4 = reinterpret_cast<const float4*>(zt)[j];
+            vt[0] = t4.x; vt[1] = t4.y; vt[2] = t4.z; vt[3] = t4.w;
+            if (residual) {
+                const float4 d4 = reinterpret_cast<const float4*>(zd)[j];
+                vd[0] = d4.x; vd[1] = d4.y; vd[2] = d4.z; vd[3] = d4.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = min(4 * j + e, V - 1);
+                vt[e] = zt[x];
+                if (residual) vd[e] = zd[x];
+            }
+        }
         philox4x32_10(w0, w1, w2, w3, k0, k1);
         const uint32_t w[4] = {w0, w1, w2, w3};
 #pragma unroll
@@ -220,10 +239,10 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
             const int x = 4 * j + e;
             if (x >= V) break;
             const float E = -__builtin_amdgcn_logf(philox_uniform(w[e])) * kLn2;
-            const float pt = __builtin_amdgcn_exp2f(fmaf(zt[x], c1, -ct)) * rst;
+            const float pt = __builtin_amdgcn_exp2f(fmaf(vt[e], c1, -ct)) * rst;
             if (pt > 0.f) race_merge(bp, {E * __builtin_amdgcn_rcpf(pt), x});
             if (residual) {
-                const float pd = __builtin_amdgcn_exp2f(fmaf(zd[x], c1, -cd)) * rsd;
+                const float pd = __builtin_amdgcn_exp2f(fmaf(vd[e], c1, -cd)) * rsd;
                 const float rr = pt - pd;
                 if (rr > 0.f) race_merge(br, {E * __builtin_amdgcn_rcpf(rr), x});
             }
