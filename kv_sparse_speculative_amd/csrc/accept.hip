@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a
         for (; j + 3 * kStatThreads < u1; j += 4 * kStatThreads) {
             float4 v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = z4[j + q * kStatThreads];
+            for (int q = 0; q < 4; ++q) v[q] = load_stream_f4(z4 + j + q * kStatThreads);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int x = 4 * (j + q * kStatThreads);
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a
             }
         }
         for (; j < u1; j += kStatThreads) {
-            const float4 v = z4[j];
+            const float4 v = load_stream_f4(z4 + j);
             visit(v.x, 4 * j); visit(v.y, 4 * j + 1); visit(v.z, 4 * j + 2); visit(v.w, 4 * j + 3);
         }
     } else {
@@ -218,10 +218,10 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
                  w2 = (uint32_t)b, w3 = off;
         float vt[4], vd[4] = {0.f, 0.f, 0.f, 0.f};
         if (vec) {
-            const float4 t4 = reinterpret_cast<const float4*>(zt)[j];
+            const float4 t4 = load_stream_f4(reinterpret_cast<const float4*>(zt) + j);
             vt[0] = t4.x; vt[1] = t4.y; vt[2] = t4.z; vt[3] = t4.w;
             if (residual) {
-                const float4 d4 = reinterpret_cast<const float4*>(zd)[j];
+                const float4 d4 = load_stream_f4(reinterpret_cast<const float4*>(zd) + j);
                 vd[0] = d4.x; vd[1] = d4.y; vd[2] = d4.z; vd[3] = d4.w;
             }
         } else {

@@ -62,6 +62,8 @@ template <int D, bool GATHER, int NRT>
 __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
     using C = MfmaCfg<D, NRT>;
     constexpr int KS = C::KS, DT = C::DT, STRIDE = C::STRIDE, ROWS = C::ROWS;
+    constexpr int kLPR = D / 8;            // lanes per V row (16 B each)
+    constexpr int kRPI = 64 / kLPR;        // V rows per load instruction (KS * kRPI = 16)
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
     __shared__ int s_bad;
 
@@ -212,8 +214,15 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
                 const size_t off = (size_t)(ok ? row : 0u) * D + q4 * 8;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
+                    // K in MFMA operand order: an instruction covers 64 B of each of 16 rows,
+                    // which plain loads serve best (the caches merge the two halves of a line)
                     kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32);
-                    vr[kt][ks] = *reinterpret_cast<const uint4*>(vp + off + ks * 32);
+                    // V goes through LDS, so it is read row-contiguously: instruction ks covers
+                    // whole rows kRPI * ks .. + kRPI - 1 of the tile with nontemporal loads
+                    const int j = ks * kRPI + lane / kLPR;
+                    const unsigned vrow = (unsigned)__shfl((int)row, j);
+                    const bool vok = (okm[kt] >> j) & 1u;
+                    vr[kt][ks] = load_stream(vp + (size_t)(vok ? vrow : 0u) * D + (lane % kLPR) * 8);
                 }
             }
         };
@@ -223,11 +232,13 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
             wave_lds_order();
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const bool ok = (okm[kt] >> m16) & 1u;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    *reinterpret_cast<uint4*>(vl + (kt * 16 + m16) * STRIDE + ks * 32 + q4 * 8) =
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int j = ks * kRPI + lane / kLPR;           // row of the tile this lane read
+                    const bool ok = (okm[kt] >> j) & 1u;
+                    *reinterpret_cast<uint4*>(vl + (kt * 16 + j) * STRIDE + (lane % kLPR) * 8) =
                         ok ? vr[kt][ks] : make_uint4(0, 0, 0, 0);
+                }
             }
 
             // S^T = K . Q^T : C tile [key 4*q4+i][row m16].

@@ -36,8 +36,8 @@ __global__ __launch_bounds__(kCopyThreads) void kv_append_kernel(AppendArgs a) {
         const int g = j / row16, c = j % row16;
         const size_t src = (((size_t)b * a.Hkv + g) * a.T + t) * row16 + c;
         const size_t dst = (((size_t)blk * a.Hkv + g) * a.bs + pos % a.bs) * row16 + c;
-        if (which) vc[dst] = vn[src];
-        else kc[dst] = kn[src];
+        if (which) vc[dst] = load_stream(vn + src);
+        else kc[dst] = load_stream(kn + src);
     }
 }
 
@@ -91,8 +91,8 @@ __global__ __launch_bounds__(kCopyThreads) void compact_build_kernel(CompactArgs
         if (dst == kNoRow) continue;
         uint4 kv = nan4, vv = nan4;
         if (src != kNoRow) {
-            kv = ks[(size_t)src * row16 + c];
-            vv = vs[(size_t)src * row16 + c];
+            kv = load_stream(ks + (size_t)src * row16 + c);
+            vv = load_stream(vs + (size_t)src * row16 + c);
         }
         kd[(size_t)dst * row16 + c] = kv;
         vd[(size_t)dst * row16 + c] = vv;

@@ -40,6 +40,20 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Compiler-level memory barrier: keeps LDS stores and the loads that read them (from other
 // lanes of the same wave) in program order; the LDS unit executes one wave's DS instructions
 // in order, so no hardware wait is needed between them.
+// 16-byte load of data the call reads exactly once (K/V rows, logits): a nontemporal load.
+// On gfx950 a stream of these keeps ~7.1 TB/s of HBM read rate, against ~6.2 TB/s for plain
+// loads that allocate in the caches.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    const u32x4_t t = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float4 load_stream_f4(const void* p) {
+    const uint4 u = load_stream(p);
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                       __uint_as_float(u.w));
+}
+
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
 // Physical row address of logical position `pos` of (sequence, KV head) in the paged cache.

@@ -97,7 +97,7 @@ __device__ __forceinline__ void load_k(const uint16_t* kp, const unsigned* tab, 
         const size_t off = (size_t)(ok ? row : 0u) * D + q4 * 8;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
-            kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32);
+            kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32);   // 64 B per row: plain
     }
 }
 

@@ -1,6 +1,6 @@
-// Measurement reference: a plain read-only stream over a device buffer with 16-byte loads,
-// the practical HBM read ceiling the attention kernels are compared against (besides the
-// vendor peak). Not part of the method.
+// Measurement reference: a read-only stream over a device buffer with 16-byte nontemporal
+// loads, the practical HBM read ceiling the attention kernels are compared against (besides
+// the vendor peak). Not part of the method.
 
 #include "common.h"
 #include "launch.h"
@@ -20,13 +20,13 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
     for (; i + (kStreamUnroll - 1) * kStreamThreads < n; i += stride) {
         uint4 v[kStreamUnroll];
 #pragma unroll
-        for (int u = 0; u < kStreamUnroll; ++u) v[u] = p[i + u * kStreamThreads];
+        for (int u = 0; u < kStreamUnroll; ++u) v[u] = load_stream(p + i + u * kStreamThreads);
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u)                // tail of fewer than a full batch
-        if (i + u * kStreamThreads < n) acc ^= p[i + u * kStreamThreads].x;
+        if (i + u * kStreamThreads < n) acc ^= load_stream(p + i + u * kStreamThreads).x;
     if (acc == 0x9e3779b9u) sink[0] = acc;               // keeps the loads live
 }
 
