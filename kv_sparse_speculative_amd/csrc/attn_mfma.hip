@@ -21,7 +21,10 @@
 //       each lane owns one query row of the C tile);
 //     O^T (16 dims x 16 rows) += V^T . P^T with P split into bf16 hi + lo parts (two MFMAs) so
 //       that P carries ~16 mantissa bits; V^T is read transposed from a padded LDS tile that
-//       the same wave wrote.
+//       the same wave wrote V rows arrive
+//       with row-contiguous nontemporal loads (each instruction covers whole rows, the pattern
+//       that keeps the HBM read rate highest); K rows, used straight from registers as the
+//       MFMA operand, keep plain loads (routing K through LDS as well measured slower).
 // Waves merge (max, sum, O) through LDS; with one split the workgroup writes the final
 // normalised output, otherwise (m, l, o) partials that the merge kernel combines.
 
