@@ -290,7 +290,20 @@ __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
         return;
     }
     const float* c = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
-    for (int j = tid; j < n; j += 1024) lds_scores[j + (j >> 5)] = c[j];
+    {
+        // all of a thread's loads are issued before any is waited on (n <= 1024 * MAXC)
+        float tmp[MAXC];
+#pragma clang loop unroll(full)
+        for (int q = 0; q < MAXC; ++q) {
+            const int j = tid + q * 1024;
+            tmp[q] = j < n ? c[j] : 0.f;
+        }
+#pragma clang loop unroll(full)
+        for (int q = 0; q < MAXC; ++q) {
+            const int j = tid + q * 1024;
+            if (j < n) lds_scores[j + (j >> 5)] = tmp[q];
+        }
+    }
     __syncthreads();
 
     const int C = (n + 1023) / 1024;
