@@ -189,7 +189,7 @@ KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads
  *     offset low 32 bits); stream 0 word 0 gives u_i, stream 1 word x % 4 of block x / 4
  *     gives u'_x; a 32-bit word x maps to (x >> 9) * 2^-23 + 2^-24. Callers advance `offset`
  *     between calls that share a seed.
- *   Limits: 0 <= gamma <= 31 (KVSS_EUNSUPPORTED above), 1 <= vocab < 2^24.
+ *   Limits: 0 <= gamma <= 31 and batch <= 65535 (KVSS_EUNSUPPORTED above), 1 <= vocab < 2^24.
  *   out_tokens       int32 [batch, gamma + 1]: emitted tokens, then -1.
  *   out_num_accepted int32 [batch]: accepted draft tokens, 0 .. gamma.
  *   row_stats        float32 [batch, 2 * gamma + 1, 4] or NULL: per logit row (target rows
@@ -232,12 +232,13 @@ KVSS_API int draft_attn_topk(const kvss_kv* kv, const void* q, int num_q_heads, 
  * [batch, vocab] (fp32): temperature 0 takes the argmax (ties to the lowest id); temperature
  * t > 0 draws from softmax(logits / t) by the exponential race spec_accept uses, on a Philox
  * stream of its own (stream 2, position `step`, same key and offset conventions), so the draft
- * token and the later acceptance draws are independent. The same statistics kernel as
- * spec_accept's row statistics streams each row once.
+ * token and the later acceptance draws are independent. The normaliser of softmax is common to
+ * every token, so the race winner is argmin_x (ln E_x - z_x / t) and each row is read once.
  *   step       draft step index within the round, in [0, 65535]
  *   tokens     int32 [batch] (device), written
  *   row_stats  nullable float [batch, 4]: max of z / t, sum of exp(z / t - max), 0, argmax
- * Workspace: kvss_sample_workspace_bytes(batch, vocab). vocab < 2^24.
+ * Workspace: kvss_sample_workspace_bytes(batch, vocab). vocab < 2^24; batch <= 65535
+ * (KVSS_EUNSUPPORTED above).
  */
 KVSS_API size_t kvss_sample_workspace_bytes(int batch, int vocab);
 KVSS_API int draft_sample(const float* logits, int batch, int vocab, float temperature,

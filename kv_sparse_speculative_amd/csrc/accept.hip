@@ -12,8 +12,6 @@
 //            over one slice of the emitting row, w = max(0, p - q) after a rejection (p if that
 //            is all zero) or p after full acceptance; re-reads only that row pair;
 //   finalize (sampling only) one wave per sequence: the winning token of the slices.
-// With gamma = 0 the same kernels sample one token per sequence from a single logit row (the
-// draft-token sampler): stats, an empty accept walk, and the race over that row.
 
 #include "common.h"
 #include "launch.h"
@@ -23,6 +21,7 @@ namespace {
 
 constexpr int kStatThreads = 256;
 constexpr int kRaceThreads = 256;
+constexpr uint32_t kRaceStream = 1;     // Philox stream of the race uniforms
 
 struct Part {          // per (sequence, row, slice)
     float m, s, zmax;
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
     const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(zt) & 15) == 0 &&
                      (!residual || (reinterpret_cast<uintptr_t>(zd) & 15) == 0);
     for (int j = j0 + tid; j < j1; j += kRaceThreads) {
-        uint32_t w0 = (uint32_t)j, w1 = ((uint32_t)a.race_stream << 16) | (uint32_t)(a.pos_base + pos),
+        uint32_t w0 = (uint32_t)j, w1 = ((uint32_t)kRaceStream << 16) | (uint32_t)pos,
                  w2 = (uint32_t)b, w3 = off;
         float vt[4], vd[4] = {0.f, 0.f, 0.f, 0.f};
         if (vec) {

@@ -50,7 +50,6 @@ constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes
 constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
 constexpr int kMaxGamma = 31;      // speculation length limit of spec_accept
 constexpr int kMaxGridYZ = 65535;  // batch and KV heads index the y / z grid dimensions
-constexpr int kRaceStream = 1;     // Philox stream of the acceptance race
 constexpr int kDraftStream = 2;    // Philox stream of the draft-token race
 
 struct Plan {
@@ -366,6 +365,7 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
     if (batch < 0) return fail(KVSS_EINVAL, "batch must be >= 0");
     if (gamma < 0) return fail(KVSS_EINVAL, "gamma must be >= 0");
     if (gamma > kMaxGamma) return fail(KVSS_EUNSUPPORTED, "gamma %d exceeds %d", gamma, kMaxGamma);
+    if (batch > kMaxGridYZ) return fail(KVSS_EUNSUPPORTED, "batch must be <= %d", kMaxGridYZ);
     if (vocab <= 0 || vocab >= (1 << 24)) return fail(KVSS_EINVAL, "vocab must be in [1, 2^24)");
     if (!temperature_ok(temperature))
         return fail(KVSS_EINVAL, "temperature must be finite and 0 or >= 1 / FLT_MAX");
@@ -391,48 +391,42 @@ int spec_accept(const float* target_logits, const float* draft_logits, const int
     a.stats = row_stats;
     a.out_tokens = out_tokens;
     a.out_num = out_num_accepted;
-    a.race_stream = kRaceStream;
-    a.pos_base = 0;
     return hip_status(kvss::launch_accept(a, workspace, static_cast<hipStream_t>(stream)),
                       "accept launch");
 }
 
 size_t kvss_sample_workspace_bytes(int batch, int vocab) {
     if (batch < 0 || vocab <= 0) return 0;
-    return kvss_accept_workspace_bytes(batch, 0, vocab) + align_up((size_t)batch * sizeof(int32_t));
+    return align_up(kvss::sample_workspace_bytes(batch, vocab));
 }
 
 int draft_sample(const float* logits, int batch, int vocab, float temperature, uint64_t seed,
                  uint64_t offset, int step, int32_t* tokens, float* row_stats, void* workspace,
                  size_t workspace_bytes, void* stream) {
     if (batch < 0) return fail(KVSS_EINVAL, "batch must be >= 0");
+    if (batch > kMaxGridYZ) return fail(KVSS_EUNSUPPORTED, "batch must be <= %d", kMaxGridYZ);
     if (vocab <= 0 || vocab >= (1 << 24)) return fail(KVSS_EINVAL, "vocab must be in [1, 2^24)");
     if (!temperature_ok(temperature))
         return fail(KVSS_EINVAL, "temperature must be finite and 0 or >= 1 / FLT_MAX");
     if (step < 0 || step > 0xffff) return fail(KVSS_EINVAL, "step must be in [0, 65535]");
     if (batch == 0) return ok();
     if (!logits || !tokens) return fail(KVSS_EINVAL, "logits and tokens must be non-NULL");
-    const size_t acc = kvss_accept_workspace_bytes(batch, 0, vocab);
     const size_t need = kvss_sample_workspace_bytes(batch, vocab);
     if (workspace_bytes < need || !workspace)
         return fail(KVSS_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                     workspace_bytes, need);
-    // One logit row per sequence is the gamma = 0 acceptance problem: an empty accept walk
-    // and the race over that row, on the draft's own Philox stream at position `step`.
-    kvss::AcceptArgs a{};
-    a.target = logits;
+    kvss::SampleArgs a{};
+    a.logits = logits;
     a.B = batch;
-    a.gamma = 0;
     a.V = vocab;
     a.inv_temp = temperature > 0.f ? (float)(1.0 / (double)temperature) : 0.f;
     a.seed = seed;
     a.offset = offset;
+    a.stream_id = kDraftStream;
+    a.step = step;
+    a.tokens = tokens;
     a.stats = row_stats;
-    a.out_tokens = tokens;
-    a.out_num = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + acc);
-    a.race_stream = kDraftStream;
-    a.pos_base = step;
-    return hip_status(kvss::launch_accept(a, workspace, static_cast<hipStream_t>(stream)),
+    return hip_status(kvss::launch_sample(a, workspace, static_cast<hipStream_t>(stream)),
                       "draft sample launch");
 }
 

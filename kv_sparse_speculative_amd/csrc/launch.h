@@ -112,8 +112,6 @@ struct AcceptArgs {
     float* stats;               // [B, 2*gamma+1, 4] or null
     int32_t* out_tokens;        // [B, gamma+1]
     int32_t* out_num;           // [B]
-    int race_stream;            // Philox stream of the exponential race
-    int pos_base;               // added to the emitting position in the race counter
 };
 
 // Workspace carve-up of one acceptance call: per-row slice partials, per-sequence decisions,
@@ -124,6 +122,20 @@ struct AcceptPlan {
 };
 AcceptPlan accept_plan(int B, int gamma, int V);
 hipError_t launch_accept(const AcceptArgs& a, void* workspace, hipStream_t s);
+
+// Draft-token sampler: one logit row per sequence, one pass (slice kernel + finalize).
+struct SampleArgs {
+    const float* logits;        // [B, V]
+    int B, V;
+    float inv_temp;             // 0 => greedy
+    uint64_t seed, offset;
+    int stream_id, step;        // Philox stream and position of the race
+    int32_t* tokens;            // [B]
+    float* stats;               // [B, 4] or null
+};
+int sample_slices(int V);
+size_t sample_workspace_bytes(int B, int V);
+hipError_t launch_sample(const SampleArgs& a, void* workspace, hipStream_t s);
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 

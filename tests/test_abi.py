@@ -109,6 +109,8 @@ def test_accept_and_streaming_validation():
     assert L.spec_accept(*bad) == kvss.KVSS_EINVAL
     bad = list(args); bad[1] = None
     assert L.spec_accept(*bad) == kvss.KVSS_EINVAL                         # temperature > 0 needs q
+    bad = list(args); bad[3] = 65536
+    assert L.spec_accept(*bad) == kvss.KVSS_EUNSUPPORTED                   # grid z holds the batch
     assert L.kvss_accept_workspace_bytes(4, 3, 100) >= 4 * 7 * 16
     assert L.kvss_streaming_set(FAKE, 2, 2, -1, 4, FAKE, FAKE, FAKE, None) == kvss.KVSS_EINVAL
     assert L.kvss_streaming_set(None, 2, 2, 4, 4, FAKE, FAKE, FAKE, None) == kvss.KVSS_EINVAL
@@ -166,6 +168,7 @@ def test_draft_sample_and_topk_validation():
     assert smp(ws=None) == kvss.KVSS_EWORKSPACE
     assert smp(wsb=8) == kvss.KVSS_EWORKSPACE
     assert smp(B=0) == kvss.KVSS_OK
+    assert smp(B=65536) == kvss.KVSS_EUNSUPPORTED
     assert lib.kvss_sample_workspace_bytes(4, 1000) > 0
     d = _desc()
     topk = lambda d=d, Hq=8, k=16, ws=FAKE, wsb=1 << 30: lib.draft_attn_topk(

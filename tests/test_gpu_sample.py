@@ -46,6 +46,11 @@ def test_draft_sample_matches_oracle(name, batch, vocab, temp):
         np.testing.assert_array_equal(g, ref)
         return
     np.testing.assert_allclose(host(st)[:, 0], z.max(axis=1) / temp, rtol=1e-6)
+    # sum of exp(z / t - max): float32 terms summed over the row, relative error << 1e-4
+    y = z / temp
+    ref_s = np.exp(y - y.max(axis=1, keepdims=True)).sum(axis=1)
+    np.testing.assert_allclose(host(st)[:, 1], ref_s, rtol=1e-4)
+    assert (host(st)[:, 2] == 0).all()
     bad = [b for b in range(batch) if g[b] != ref[b] and not _near_tie(z[b], temp, seed, offset, b, step)]
     near = sum(1 for b in range(batch) if g[b] != ref[b]) - len(bad)
     print(f"draft sample {name} V={z.shape[1]} t={temp}: near-tie flips {near}")
@@ -64,3 +69,30 @@ def test_draft_sample_step_and_stream_change_the_draw():
     torch.cuda.synchronize()
     assert (host(a) != host(b)).mean() > 0.9
     assert (host(a) != host(c)[:, 0]).mean() > 0.9
+
+
+@pytest.mark.parametrize("vocab,shift", [(1001, 0), (4096, 1), (9000, 3)],
+                         ids=["ragged_vocab", "unaligned_rows", "ragged_two_slices"])
+@pytest.mark.parametrize("temp", [0.0, 1.0])
+def test_draft_sample_scalar_path(vocab, shift, temp):
+    """Rows that are not whole 16-byte blocks (vocab % 4 != 0, or a base 4 bytes past 16-byte
+    alignment) take the element-wise path; tokens and statistics still match the oracle."""
+    ns = generate(WORKLOADS["llama8b_ctx8k"], device="cuda", batch=9, parts=("accept",), vocab=vocab)
+    src = ns.draft_logits[:, 0].contiguous()
+    buf = torch.empty(src.numel() + 4, dtype=torch.float32, device="cuda")
+    logits = buf[shift:shift + src.numel()].view(src.shape)
+    logits.copy_(src)
+    seed, offset, step = 123, 7, 3
+    tok, st = kvss.draft_sample(logits, temp, seed, offset, step, want_stats=True)
+    torch.cuda.synchronize()
+    z = host(src).astype(np.float64)
+    ref = oacc.draft_sample(z, temp, seed, offset, step)
+    g = host(tok)
+    np.testing.assert_array_equal(host(st)[:, 3].astype(np.int64), [oacc.argmax_lowest(r) for r in z])
+    if temp == 0:
+        np.testing.assert_array_equal(g, ref)
+        return
+    ref_s = np.exp(z / temp - (z / temp).max(axis=1, keepdims=True)).sum(axis=1)
+    np.testing.assert_allclose(host(st)[:, 1], ref_s, rtol=1e-4)
+    bad = [b for b in range(9) if g[b] != ref[b] and not _near_tie(z[b], temp, seed, offset, b, step)]
+    assert not bad, bad
