@@ -64,6 +64,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 template <int D, bool GATHER, int NRT>
 __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
     using C = MfmaCfg<D, NRT>;
+    constexpr int NBUF = 2;            // chunks in flight per wave
     constexpr int KS = C::KS, DT = C::DT, STRIDE = C::STRIDE, ROWS = C::ROWS;
     constexpr int kLPR = D / 8;            // lanes per V row (16 B each)
     constexpr int kRPI = 64 / kLPR;        // V rows per load instruction (KS * kRPI = 16)
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     __shared__ int s_bad;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
+    const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m16 = lane & 15, q4 = lane >> 4;
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     if (tid == 0) s_bad = 0;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     const uint16_t* vp = static_cast<const uint16_t*>(a.v);
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-    const int bs = a.bs;
+    const int bs = a.bs, sh = (bs & (bs - 1)) == 0 ? __builtin_ctz(bs) : -1;
 
     // Q^T as the B operand: lane supplies column (row) rt*16 + m16, dims ks*32 + q4*8 .. +7.
     bf16x8 qop[NRT][KS];
@@ -106,10 +107,14 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
                 qop[rt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + ks * 32));
             limit[rt] = GATHER ? 0x7fffffff : L - a.T + t;
         } else {
+            // zero queries: finite scores, never written out, and no causal bound
+            limit[rt] = 0x7fffffff;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
         }
     }
+    // Every key below this position is visible to every query row (the first causal row).
+    const int lim_all = GATHER ? 0x7fffffff : L - a.T;
 
     f32x4 o[DT][NRT];
 #pragma unroll
@@ -196,36 +201,54 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
         }
         __syncthreads();
 
-        // Issue the K/V loads of one 32-key chunk into registers.
+        // Issue the K/V loads of one 32-key chunk into registers. okm[kt] has bit i set when
+        // key c0 + 16 kt + i is a valid cache row. Masked keys load cache row 0 (always a valid
+        // address) and are discarded: their scores become -inf and their V rows are zeroed
+        // when consumed.
+        // K in MFMA operand order: an instruction covers 64 B of each of 16 rows, which plain
+        // loads serve best (the caches merge the two halves of a line). V goes through LDS, so
+        // it is read row-contiguously: instruction ks covers whole rows kRPI * ks .. + kRPI - 1
+        // of the tile with nontemporal loads.
         auto issue = [&](int c0, uint4 (&kr)[2][KS], uint4 (&vr)[2][KS], unsigned (&okm)[2]) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const int v = c0 + kt * 16 + m16;
-                unsigned row = kInvalidRow;
-                if (v < seg_end) {
-                    if constexpr (GATHER) {
-                        row = rowtab[v - seg];
-                    } else {
-                        const unsigned base = rowtab[v / bs - blk0];
-                        row = base == kInvalidRow ? kInvalidRow : base + (unsigned)(v % bs);
-                    }
-                }
-                const bool ok = row != kInvalidRow;
-                okm[kt] = (unsigned)(__ballot(ok) & 0xffffull);
-                // Masked keys load cache row 0 (always a valid address) and are discarded:
-                // their scores become -inf and their V rows are zeroed when consumed.
-                const size_t off = (size_t)(ok ? row : 0u) * D + q4 * 8;
+                const int t0 = c0 + kt * 16;                          // wave-uniform
+                if constexpr (GATHER) {
+                    const int v = t0 + m16;
+                    const unsigned row = v < seg_end ? rowtab[v - seg] : kInvalidRow;
+                    const bool ok = row != kInvalidRow;
+                    okm[kt] = (unsigned)(__ballot(ok) & 0xffffull);
+                    const size_t off = (size_t)(ok ? row : 0u) * D + q4 * 8;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    // K in MFMA operand order: an instruction covers 64 B of each of 16 rows,
-                    // which plain loads serve best (the caches merge the two halves of a line)
-                    kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32);
-                    // V goes through LDS, so it is read row-contiguously: instruction ks covers
-                    // whole rows kRPI * ks .. + kRPI - 1 of the tile with nontemporal loads
-                    const int j = ks * kRPI + lane / kLPR;
-                    const unsigned vrow = (unsigned)__shfl((int)row, j);
-                    const bool vok = (okm[kt] >> j) & 1u;
-                    vr[kt][ks] = load_stream(vp + (size_t)(vok ? vrow : 0u) * D + (lane % kLPR) * 8);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32);
+                        const int j = ks * kRPI + lane / kLPR;
+                        const unsigned vrow = (unsigned)__shfl((int)row, j);
+                        const bool vok = (okm[kt] >> j) & 1u;
+                        vr[kt][ks] = load_stream(vp + (size_t)(vok ? vrow : 0u) * D + (lane % kLPR) * 8);
+                    }
+                } else {
+                    // Chunks start on multiples of 16 and the block size is a multiple of 16,
+                    // so the tile's 16 keys are consecutive rows of one block: one uniform
+                    // table read gives them all.
+                    unsigned r0 = 0;
+                    int n_ok = 0;
+                    if (t0 < seg_end) {
+                        const int blk = div_bs(t0, bs, sh);
+                        const unsigned base = __builtin_amdgcn_readfirstlane(rowtab[blk - blk0]);
+                        if (base != kInvalidRow) {
+                            r0 = base + (unsigned)(t0 - blk * bs);
+                            n_ok = min(seg_end - t0, 16);
+                        }
+                    }
+                    okm[kt] = n_ok >= 16 ? 0xffffu : ((1u << n_ok) - 1u);
+                    const uint16_t* kq = kp + (size_t)(m16 < n_ok ? r0 + m16 : 0u) * D + q4 * 8;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        kr[kt][ks] = *reinterpret_cast<const uint4*>(kq + ks * 32);
+                        const int j = ks * kRPI + lane / kLPR;
+                        vr[kt][ks] = load_stream(vp + (size_t)(j < n_ok ? r0 + j : 0u) * D + (lane % kLPR) * 8);
+                    }
                 }
             }
         };
@@ -258,28 +281,53 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
                     sacc[kt][rt] = acc;
                 }
 
+            // A full chunk (all 32 keys valid and visible to every row) skips the masks and
+            // keeps its reference maximum unless a score exceeds it by more than kLazyMax
+            // (log2 units): then p <= 2^kLazyMax, well inside float and the hi + lo split, and
+            // O is rescaled only when the maximum has really moved.
+            constexpr float kLazyMax = 16.f;
+            const bool full = (okm[0] & okm[1]) == 0xffffu && c0 + 31 <= lim_all;
             bf16x8 phi[NRT], plo[NRT];
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 float sv[8];
                 float cmax = kNegInf;
+                if (full) {
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+                    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = kt * 16 + q4 * 4 + i;
-                        bool allowed = (okm[kt] >> (q4 * 4 + i)) & 1u;
-                        if constexpr (!GATHER) allowed = allowed && (c0 + key <= limit[rt]);
-                        const float x = allowed ? sacc[kt][rt][i] * a.scale_log2 : kNegInf;
-                        sv[kt * 4 + i] = x;
-                        cmax = fmaxf(cmax, x);
-                    }
+                        for (int i = 0; i < 4; ++i) {
+                            const float x = sacc[kt][rt][i] * a.scale_log2;
+                            sv[kt * 4 + i] = x;
+                            cmax = fmaxf(cmax, x);
+                        }
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int key = kt * 16 + q4 * 4 + i;
+                            bool allowed = (okm[kt] >> (q4 * 4 + i)) & 1u;
+                            if constexpr (!GATHER) allowed = allowed && (c0 + key <= limit[rt]);
+                            const float x = allowed ? sacc[kt][rt][i] * a.scale_log2 : kNegInf;
+                            sv[kt * 4 + i] = x;
+                            cmax = fmaxf(cmax, x);
+                        }
+                }
                 cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
                 cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-                const float mnew = fmaxf(mrow[rt], cmax);
-                const float muse = (mnew == kNegInf) ? 0.f : mnew;
-                const float alpha = __builtin_amdgcn_exp2f(mrow[rt] - muse);
-                mrow[rt] = mnew;
+                // the first chunk of a row always moves its maximum (mrow = -inf)
+                const bool move = full ? cmax > mrow[rt] + kLazyMax : cmax > mrow[rt];
+                if (__ballot(move) != 0ull) {
+                    const float mnew = fmaxf(mrow[rt], cmax);
+                    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+                    const float alpha = __builtin_amdgcn_exp2f(mrow[rt] - muse);
+                    mrow[rt] = mnew;
+                    lrow[rt] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+                }
+                const float muse = (mrow[rt] == kNegInf) ? 0.f : mrow[rt];
                 float psum = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -289,9 +337,7 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
                     plo[rt][j] = (__bf16)(p - (float)hi);
                     psum += p;
                 }
-                lrow[rt] = lrow[rt] * alpha + psum;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+                lrow[rt] += psum;
             }
 
             // O^T += V^T . P^T. k-slot j of lane group q4 is key 16*(j/4) + 4*q4 + (j%4),
@@ -323,22 +369,23 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
             wave_lds_order();
         };
 
-        // Double-buffered walk over this wave's chunks with two chunks always in flight:
-        // consume A, reissue A two chunks ahead, consume B, reissue B. Issues are
-        // unconditional (a chunk past the end loads a dummy row and is fully masked) and the
-        // loop condition is the only exit, so every consume is reached with the same loads
-        // outstanding and the compiler's wait covers only the chunk being consumed.
+        // Walk over this wave's chunks with NBUF chunks always in flight: consume buffer i,
+        // reissue it NBUF chunks ahead, move to buffer i + 1. Issues are unconditional (a
+        // chunk past the end loads a dummy row and is fully masked) and the loop condition is
+        // the only exit, so every consume is reached with the same loads outstanding and the
+        // compiler's wait covers only the chunk being consumed.
         constexpr int stride = kWaves * 32;
-        uint4 kA[2][KS], vA[2][KS], kB[2][KS], vB[2][KS];
-        unsigned okA[2], okB[2];
+        uint4 kbuf[NBUF][2][KS], vbuf[NBUF][2][KS];
+        unsigned okbuf[NBUF][2];
         int c = seg + wid * 32;
-        issue(c, kA, vA, okA);
-        issue(c + stride, kB, vB, okB);
-        for (; c < seg_end; c += 2 * stride) {
-            consume(c, kA, vA, okA);
-            issue(c + 2 * stride, kA, vA, okA);
-            consume(c + stride, kB, vB, okB);
-            issue(c + 3 * stride, kB, vB, okB);
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) issue(c + i * stride, kbuf[i], vbuf[i], okbuf[i]);
+        for (; c < seg_end; c += NBUF * stride) {
+#pragma unroll
+            for (int i = 0; i < NBUF; ++i) {
+                consume(c + i * stride, kbuf[i], vbuf[i], okbuf[i]);
+                issue(c + (i + NBUF) * stride, kbuf[i], vbuf[i], okbuf[i]);
+            }
         }
     }
 

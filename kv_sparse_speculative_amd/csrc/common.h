@@ -56,6 +56,9 @@ __device__ __forceinline__ float4 load_stream_f4(const void* p) {
 
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
+// x / bs with a shift when the block size is a power of two (sh >= 0), else a division.
+__device__ __forceinline__ int div_bs(int x, int bs, int sh) { return sh >= 0 ? x >> sh : x / bs; }
+
 // Physical row address of logical position `pos` of (sequence, KV head) in the paged cache.
 // Returns false when the block id read from the table is outside [0, num_blocks).
 struct PagedCache {

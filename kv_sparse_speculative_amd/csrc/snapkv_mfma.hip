@@ -76,9 +76,6 @@ __device__ bool stage_blocks(const SnapArgs& a, int b, int g, int k0, int k1, un
     return bad;
 }
 
-// x / bs with a shift when the block size is a power of two (sh >= 0), else a division.
-__device__ __forceinline__ int div_bs(int x, int bs, int sh) { return sh >= 0 ? x >> sh : x / bs; }
-
 // Load the K rows of one 32-key chunk (keys c0 .. c0+31, each 16 lanes x 16 B) into registers.
 // c0 is wave-uniform and a multiple of 16, so each 16-key tile's block base is one uniform LDS
 // read. Keys outside [k0, k1) or with a bad block load row 0 and are reported as masked.
