@@ -268,7 +268,8 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
 //   2. thread t takes the contiguous positions [t*C, t*C + C) plus the pool halo from LDS and
 //      keeps the pooled values in registers;
 //   3. four MSB-first radix passes count digits into per-wave LDS histograms (no cross-wave
-//      contention) and pick the digit of the k-th largest with one block scan;
+//      contention; each thread adds runs of equal digits once) and pick the digit of the k-th
+//      largest with one block scan;
 //   4. an ordered compaction writes the kept positions.
 constexpr int kPoolHalo = 3;   // register path: pool kernels up to 2 * kPoolHalo + 1
 constexpr int kTopkWaves = 16;
@@ -334,11 +335,24 @@ __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
         const int shift = 24 - 8 * pass;
         for (int t = tid; t < kTopkWaves * 256; t += 1024) whist[t] = 0;
         __syncthreads();
+        // A thread's positions are consecutive, and pooled scores of neighbouring positions
+        // mostly share their high digits: count runs of one digit in registers and add each
+        // run once, so the waves' atomics rarely collide on one histogram word.
+        unsigned cur = 0u, run = 0u;
 #pragma clang loop unroll(full)
         for (int e = 0; e < MAXC; ++e) {
             const unsigned u = __float_as_uint(win[e]);
-            if (live(e) && (u & mask) == prefix) atomicAdd(&whist[wid * 256 + ((u >> shift) & 255u)], 1u);
+            const unsigned bin = (u >> shift) & 255u;
+            if (live(e) && (u & mask) == prefix) {
+                if (bin != cur && run != 0u) {
+                    atomicAdd(&whist[wid * 256 + cur], run);
+                    run = 0u;
+                }
+                cur = bin;
+                ++run;
+            }
         }
+        if (run != 0u) atomicAdd(&whist[wid * 256 + cur], run);
         __syncthreads();
         int cnt = 0;
         if (tid < 256) {
