@@ -4,7 +4,9 @@
 // Kernels, in launch order:
 //   stats    grid (slice, row, sequence): each workgroup streams one slice of one logit row
 //            (target rows 0..gamma, draft rows 0..gamma-1) once with 16-byte loads and writes a
-//            partial (max of z/temp, sum of exp(z/temp - max), max z, its lowest index);
+//            partial (a reference r, the sum of 2^(z log2(e) / temp - r), max z, its lowest
+//            index); the reference moves only when a term would pass 2^64, so the common block
+//            of 4 tokens costs four fma + exp2 and no data-dependent branch;
 //   decide   one wave per sequence: merges the partials into row statistics, walks the gamma
 //            accept tests (greedy argmax match, or u_i < p_i(x_i) / q_i(x_i) with Philox
 //            uniforms) and writes the accepted prefix, the count and the emitting position;
@@ -24,7 +26,9 @@ constexpr int kRaceThreads = 256;
 constexpr uint32_t kRaceStream = 1;     // Philox stream of the race uniforms
 
 struct Part {          // per (sequence, row, slice)
-    float m, s, zmax;
+    float m2;          // reference of the sum in log2 units (<= max of z * log2(e) / t)
+    float s;           // sum of 2^(z * log2(e) / t - m2)
+    float zmax;        // max z and its lowest index
     int imax;
 };
 
@@ -38,10 +42,11 @@ struct Decision {      // per sequence
     int pad[3];
 };
 
+// (reference, sum) pairs in the log2 domain
 __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
     const float M = fmaxf(m, m2);
     if (M == kNegInf) { m = kNegInf; s = 0.f; return; }
-    s = s * __expf(m - M) + s2 * __expf(m2 - M);
+    s = s * __builtin_amdgcn_exp2f(m - M) + s2 * __builtin_amdgcn_exp2f(m2 - M);
     m = M;
 }
 
@@ -59,6 +64,22 @@ __device__ __forceinline__ const float* row_ptr(const AcceptArgs& a, int b, int 
                         : a.draft + ((size_t)b * gamma + (r - gamma - 1)) * a.V;
 }
 
+// Statistics of one logit row from its slice partials: m = max of z / t (exactly (max z) / t:
+// rounding is monotone), s = sum of exp(z / t - m), and the argmax.
+__device__ __forceinline__ void row_stats(const Part* p, int nslice, float it, bool greedy,
+                                          float& m, float& s, float& best, int& bi) {
+    float m2 = kNegInf, s2 = 0.f;
+    best = kNegInf;
+    bi = 0x7fffffff;
+    for (int k = 0; k < nslice; ++k) {
+        if (!greedy) ms_merge(m2, s2, p[k].m2, p[k].s);
+        am_merge(best, bi, p[k].zmax, p[k].imax);
+    }
+    m = best * it;
+    s = 0.f;
+    if (!greedy && best != kNegInf) s = s2 * __builtin_amdgcn_exp2f(m2 - best * (it * kLog2e));
+}
+
 template <bool GREEDY>
 __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a, Part* parts,
                                                                     int nslice) {
@@ -71,15 +92,36 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a
     const int units = vec ? a.V / 4 : a.V;
     const int per = (units + nslice - 1) / nslice;
     const int u0 = slice * per, u1 = min(units, u0 + per);
-    const float it = a.inv_temp;
+    const float c = a.inv_temp * kLog2e;
     float m = kNegInf, s = 0.f, best = kNegInf;
     int bi = 0x7fffffff;
-    auto visit = [&](float zv, int x) {
-        if (zv > best) { best = zv; bi = x; }      // each thread visits increasing x
+    // Block of n <= 4 tokens x0 .. x0 + n - 1. The sum keeps a lazy reference m: a block's terms
+    // 2^(z c - m) are added as they are unless their sum leaves [0, 2^64] (a score more than 64
+    // above m, or the first block with m = -inf); only then does m move to the block's max.
+    auto visit = [&](const float (&v)[4], int x0, int n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n && v[e] > best) { best = v[e]; bi = x0 + e; }    // increasing x per thread
         if constexpr (!GREEDY) {
-            const float y = zv * it;
-            if (y > m) { s = s * __expf(m - y) + 1.f; m = y; }
-            else s += __expf(y - m);
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < n) t += __builtin_amdgcn_exp2f(fmaf(v[e], c, -m));
+            if (!(t <= 0x1p64f)) {
+                float bm = kNegInf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (e < n) bm = fmaxf(bm, v[e] * c);
+                const float mnew = fmaxf(m, bm);
+                const float ms = mnew == kNegInf ? 0.f : mnew;
+                s *= __builtin_amdgcn_exp2f(m - ms);
+                t = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (e < n) t += __builtin_amdgcn_exp2f(fmaf(v[e], c, -ms));
+                m = mnew;
+            }
+            s += t;
         }
     };
     if (vec) {
@@ -91,16 +133,20 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a
             for (int q = 0; q < 4; ++q) v[q] = load_stream_f4(z4 + j + q * kStatThreads);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int x = 4 * (j + q * kStatThreads);
-                visit(v[q].x, x); visit(v[q].y, x + 1); visit(v[q].z, x + 2); visit(v[q].w, x + 3);
+                const float w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+                visit(w, 4 * (j + q * kStatThreads), 4);
             }
         }
         for (; j < u1; j += kStatThreads) {
             const float4 v = load_stream_f4(z4 + j);
-            visit(v.x, 4 * j); visit(v.y, 4 * j + 1); visit(v.z, 4 * j + 2); visit(v.w, 4 * j + 3);
+            const float w[4] = {v.x, v.y, v.z, v.w};
+            visit(w, 4 * j, 4);
         }
     } else {
-        for (int j = u0 + tid; j < u1; j += kStatThreads) visit(z[j], j);
+        for (int j = u0 + tid; j < u1; j += kStatThreads) {
+            const float w[4] = {z[j], 0.f, 0.f, 0.f};
+            visit(w, j, 1);
+        }
     }
     for (int o = 32; o > 0; o >>= 1) {
         const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o), b2 = __shfl_xor(best, o);
@@ -113,7 +159,7 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a
     __syncthreads();
     if (tid == 0) {
         for (int w = 1; w < kStatThreads / 64; ++w) {
-            if constexpr (!GREEDY) ms_merge(m, s, sp[w].m, sp[w].s);
+            if constexpr (!GREEDY) ms_merge(m, s, sp[w].m2, sp[w].s);
             am_merge(best, bi, sp[w].zmax, sp[w].imax);
         }
         parts[(((size_t)b * rows) + r) * nslice + slice] = Part{m, s, best, bi};
@@ -129,13 +175,9 @@ __global__ __launch_bounds__(64) void accept_decide_kernel(AcceptArgs a, const P
     const int gamma = a.gamma, V = a.V;
     const bool greedy = a.inv_temp == 0.f;
     for (int r = lane; r < rows; r += 64) {
-        const Part* p = parts + ((size_t)b * rows + r) * nslice;
-        float m = kNegInf, s = 0.f, best = kNegInf;
-        int bi = 0x7fffffff;
-        for (int k = 0; k < nslice; ++k) {
-            if (!greedy) ms_merge(m, s, p[k].m, p[k].s);
-            am_merge(best, bi, p[k].zmax, p[k].imax);
-        }
+        float m, s, best;
+        int bi;
+        row_stats(parts + ((size_t)b * rows + r) * nslice, nslice, a.inv_temp, greedy, m, s, best, bi);
         float zx = 0.f;
         if (!greedy && r != gamma) {
             const int i = (r < gamma) ? r : r - gamma - 1;
@@ -188,15 +230,12 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
     const int pos = dec[b].pos;
     const bool residual = pos < gamma;
     // merged statistics of the two rows (identical arithmetic to the decide kernel)
-    float mt = kNegInf, st = 0.f, md = kNegInf, sd = 0.f;
-    {
-        const Part* pt = parts + ((size_t)b * rows + pos) * nslice;
-        for (int k = 0; k < nslice; ++k) ms_merge(mt, st, pt[k].m, pt[k].s);
-        if (residual) {
-            const Part* pd = parts + ((size_t)b * rows + gamma + 1 + pos) * nslice;
-            for (int k = 0; k < nslice; ++k) ms_merge(md, sd, pd[k].m, pd[k].s);
-        }
-    }
+    float mt, st, md = kNegInf, sd = 0.f, zm;
+    int zi;
+    row_stats(parts + ((size_t)b * rows + pos) * nslice, nslice, a.inv_temp, false, mt, st, zm, zi);
+    if (residual)
+        row_stats(parts + ((size_t)b * rows + gamma + 1 + pos) * nslice, nslice, a.inv_temp, false,
+                  md, sd, zm, zi);
     const float* zt = a.target + ((size_t)b * (gamma + 1) + pos) * V;
     const float* zd = residual ? a.draft + ((size_t)b * gamma + pos) * V : nullptr;
     // p(x) = 2^(z(x) * it * log2e - m * log2e) / s, evaluated as one FMA and one v_exp.

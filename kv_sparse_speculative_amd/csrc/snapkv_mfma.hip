@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kW * 64) void snap_rowstats_mfma(SnapArgs a) {
         uint4 qv[2][KS];
         f32x4 acc[2][2];
         read_q<KS>(qs, 0, lane, qv[0]);
-        read_q<KS>(qs, 1, lane, qv[1]);
+        if (NT > 1) read_q<KS>(qs, 1, lane, qv[1]);
         score_tile<KS, false>(qv[0], kr, acc[0]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
         uint4 qv[2][KS];
         f32x4 acc[2][2];
         read_q<KS>(qs, 0, lane, qv[0]);
-        read_q<KS>(qs, 1, lane, qv[1]);
+        if (NT > 1) read_q<KS>(qs, 1, lane, qv[1]);
         score_tile<KS, true>(qv[0], kr, acc[0]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -406,7 +406,9 @@ hipError_t launch_passes(const SnapArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const SnapArgs& a, hipStream_t s) {
-    // Row tiles rounded up to an even count (R <= 256 rows: at most 16 tiles).
+    // One row tile up to 16 rows, else row tiles rounded up to an even count (R <= 256 rows:
+    // at most 16 tiles).
+    if (a.R <= 16) return launch_passes<D, 1>(a, s);
     switch ((((a.R + 15) / 16) + 1) / 2) {
         case 1: return launch_passes<D, 2>(a, s);
         case 2: return launch_passes<D, 4>(a, s);
