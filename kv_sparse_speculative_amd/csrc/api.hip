@@ -154,8 +154,8 @@ int run_attention(kvss::AttnArgs& a, const Plan& p, bool gather, int dtype, void
 
 struct SnapLayout {
     Plan p1;
-    int R, n_stride;
-    size_t part1, scores, pooled, total;
+    int R, n_stride, xs_stride;
+    size_t part1, scores, pooled, xs, total;
 };
 
 SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_scores) {
@@ -173,7 +173,12 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     s.part1 = align_up(rows * s.R * s.p1.nsplit * 2 * sizeof(float));
     s.scores = own_scores ? align_up(rows * s.n_stride * sizeof(float)) : 0;
     s.pooled = align_up(rows * s.n_stride * sizeof(float));
-    s.total = s.part1 + s.scores + s.pooled;
+    // With few rows the first pass keeps its scaled scores (4 R bytes per candidate, written
+    // once and read once) instead of the second pass reading K again (2 D bytes per key).
+    const bool store = kv->dtype == KVSS_BF16 && s.R <= 16 && 4 * s.R < kv->head_dim;
+    s.xs_stride = (s.n_stride + 3) / 4 * 4;
+    s.xs = store ? align_up(rows * s.R * s.xs_stride * sizeof(float)) : 0;
+    s.total = s.part1 + s.scores + s.pooled + s.xs;
     return s;
 }
 
@@ -345,6 +350,9 @@ int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads, int w, 
     a.scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + L.part1);
     a.n_stride = L.n_stride;
     a.pooled = reinterpret_cast<float*>(ws + L.part1 + L.scores);
+    // (16-byte stores and loads; an unaligned workspace takes the path that re-reads K)
+    a.xs = L.xs > 0 && aligned16(ws) ? reinterpret_cast<float*>(ws + L.part1 + L.scores + L.pooled) : nullptr;
+    a.xs_stride = L.xs_stride;
     a.pool = pool_kernel;
     a.keep = budget - w;
     a.sel_idx = sel_idx;

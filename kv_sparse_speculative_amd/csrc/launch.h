@@ -53,6 +53,8 @@ struct SnapArgs {
     float* scores;              // [B, Hkv, n_stride] column scores
     int n_stride;               // max_kv_len - w
     float* pooled;              // [B, Hkv, n_stride] workspace
+    float* xs;                  // [B, Hkv, R, xs_stride] scaled candidate scores, or null
+    int xs_stride;              // n_stride rounded up to a multiple of 4
     int pool, keep;             // pool kernel, kept count budget - w
     int32_t* sel_idx;           // [B, Hkv, keep]
     int32_t* sel_count;         // [B]

@@ -114,6 +114,20 @@ __device__ __forceinline__ void score_tile(const uint4 (&qv)[KS], const uint4 (&
                 : __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(kr[kt][ks]), to_bf16x8(qv[ks]), acc[kt], 0, 0, 0);
 }
 
+// Row constant m + log2 l of observation row r of (b, g) from the pass-1 split partials (log2
+// domain): +inf for a row with no keys (it adds nothing), NaN if a split was poisoned.
+__device__ __forceinline__ float row_constant(const SnapArgs& a, int b, int g, int r) {
+    const float* pp = a.part1 + (((size_t)b * a.Hkv + g) * a.R + r) * a.nsplit1 * 2;
+    float M = kNegInf;
+    bool nan = false;
+    for (int s = 0; s < a.nsplit1; ++s) { nan |= pp[2 * s] != pp[2 * s]; M = fmaxf(M, pp[2 * s]); }
+    float lam = 0.f;
+    if (M != kNegInf)
+        for (int s = 0; s < a.nsplit1; ++s)
+            if (pp[2 * s] != kNegInf) lam += __builtin_amdgcn_exp2f(pp[2 * s] - M) * pp[2 * s + 1];
+    return nan ? __builtin_nanf("") : (lam > 0.f ? M + __log2f(lam) : __builtin_huge_valf());
+}
+
 template <int KS>
 __device__ __forceinline__ void read_q(const uint4* qs, int t, int lane, uint4 (&qv)[KS]) {
 #pragma unroll
@@ -122,8 +136,11 @@ __device__ __forceinline__ void read_q(const uint4* qs, int t, int lane, uint4 (
 
 // ---------------------------------------------------------------- pass 1: row statistics
 // NT row tiles (16 rows each, rows past R are zero queries whose statistics are not written).
-template <int D, int NT>
+// STORE (one row tile only): also write each row's scaled scores of the candidate keys
+// j < P - w to a.xs (NaN for a key whose block id is invalid), for the stored second pass.
+template <int D, int NT, bool STORE>
 __global__ __launch_bounds__(kW * 64) void snap_rowstats_mfma(SnapArgs a) {
+    static_assert(!STORE || NT == 1, "stored scores use one row tile");
     constexpr int KS = D / 32;
     constexpr int QS = NT * KS * 64 * 16;                  // queries in MFMA operand order
     constexpr int MS = 2 * kW * NT * 16 * 4;               // per-wave (max, sum), after the loop
@@ -170,6 +187,9 @@ __global__ __launch_bounds__(kW * 64) void snap_rowstats_mfma(SnapArgs a) {
     for (int t = 0; t < NT; ++t) { nm[t] = -kNegInf; lr[t] = 0.f; }
     const float sc = fabsf(a.scale_log2);
     const int causal_from = P - a.w;            // keys below it are visible to every row
+    const int nstore = min(k1, max(causal_from, 0));
+    float* xrow = STORE && m16 < a.R
+        ? a.xs + (((size_t)b * a.Hkv + g) * a.R + m16) * a.xs_stride : nullptr;
 
     // Tile t+1's products are issued before tile t's exponentials, so the matrix core and the
     // vector ALU overlap within the wave.
@@ -187,6 +207,26 @@ __global__ __launch_bounds__(kW * 64) void snap_rowstats_mfma(SnapArgs a) {
             if (t + 1 < NT) score_tile<KS, false>(qv[(t + 1) & 1], kr, acc[(t + 1) & 1]);
             if (t + 2 < NT) read_q<KS>(qs, t + 2, lane, qv[t & 1]);
             const f32x4* s = acc[t & 1];
+            if constexpr (STORE) {
+                // lane (row m16, group q4) holds keys c0 + 16 kt + 4 q4 + i of its row
+                if (xrow != nullptr) {
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+                        const int key0 = c0 + kt * 16 + q4 * 4;
+                        float x[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            x[i] = ((okm[kt] >> (q4 * 4 + i)) & 1u) ? s[kt][i] * sc : __builtin_nanf("");
+                        if (FULL || key0 + 3 < nstore) {
+                            *reinterpret_cast<float4*>(xrow + key0) = make_float4(x[0], x[1], x[2], x[3]);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (key0 + i < nstore) xrow[key0 + i] = x[i];
+                        }
+                    }
+                }
+            }
             if constexpr (FULL) {
                 // Lazy maximum: the reference -nm[t] moves only when a term could overflow the
                 // sum, i.e. when some score exceeds it by more than 64 (the tile sum then
@@ -329,21 +369,8 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
     // A operand of S = Q . K^T: lane supplies row m16 of the tile and dims q4*8.. of k-step ks,
     // which is exactly the operand-order staging used for the B operand of pass 1.
     stage_queries<D>(a, b, g, NT, qs);
-    for (int r = tid; r < NT * 16; r += kW * 64) {
-        float cr = __builtin_huge_valf();          // rows past R (or with no keys) add nothing
-        if (r < a.R) {
-            const float* pp = a.part1 + (((size_t)b * a.Hkv + g) * a.R + r) * a.nsplit1 * 2;
-            float M = kNegInf;
-            bool nan = false;
-            for (int s = 0; s < a.nsplit1; ++s) { nan |= pp[2 * s] != pp[2 * s]; M = fmaxf(M, pp[2 * s]); }
-            float lam = 0.f;
-            if (M != kNegInf)
-                for (int s = 0; s < a.nsplit1; ++s)
-                    if (pp[2 * s] != kNegInf) lam += __builtin_amdgcn_exp2f(pp[2 * s] - M) * pp[2 * s + 1];
-            cr = nan ? __builtin_nanf("") : (lam > 0.f ? M + __log2f(lam) : __builtin_huge_valf());
-        }
-        rowc[r] = -cr;                                     // negated: the exponent is one fma
-    }
+    for (int r = tid; r < NT * 16; r += kW * 64)
+        rowc[r] = r < a.R ? -row_constant(a, b, g, r) : kNegInf;   // negated: one fma per term
     __syncthreads();
 
     float* dst = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
@@ -394,9 +421,51 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- pass 2 from stored scores
+// c[j] = sum_r 2^(x[r][j] - m_r - log2 l_r) over the R <= 16 stored rows; 4 keys per thread,
+// one 16-byte load per row.
+constexpr int kStoredKeys = kW * 64 * 4;
+
+__global__ __launch_bounds__(kW * 64) void snap_colscore_stored(SnapArgs a) {
+    __shared__ float rowc[16];
+    const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
+    const int n = max(P - a.w, 0);
+    const int k0 = tile * kStoredKeys;
+    if (k0 >= n) return;
+    if (tid < a.R) rowc[tid] = -row_constant(a, b, g, tid);
+    __syncthreads();
+    const int j = k0 + 4 * tid;
+    if (j >= n) return;
+    const float* xb = a.xs + ((size_t)b * a.Hkv + g) * a.R * a.xs_stride + j;
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < a.R; ++r) {
+        const float4 x = load_stream_f4(xb + (size_t)r * a.xs_stride);
+        const float rc = rowc[r];
+        c[0] += __builtin_amdgcn_exp2f(x.x + rc);
+        c[1] += __builtin_amdgcn_exp2f(x.y + rc);
+        c[2] += __builtin_amdgcn_exp2f(x.z + rc);
+        c[3] += __builtin_amdgcn_exp2f(x.w + rc);
+    }
+    float* dst = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride + j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (j + i < n) dst[i] = c[i];
+}
+
 template <int D, int NT>
 hipError_t launch_passes(const SnapArgs& a, hipStream_t s) {
-    snap_rowstats_mfma<D, NT><<<dim3(a.nsplit1, a.Hkv, a.B), kW * 64, 0, s>>>(a);
+    if constexpr (NT == 1) {
+        if (a.xs != nullptr) {
+            snap_rowstats_mfma<D, 1, true><<<dim3(a.nsplit1, a.Hkv, a.B), kW * 64, 0, s>>>(a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess || a.n_stride == 0) return e;
+            const dim3 grid((a.n_stride + kStoredKeys - 1) / kStoredKeys, a.Hkv, a.B);
+            snap_colscore_stored<<<grid, kW * 64, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
+    snap_rowstats_mfma<D, NT, false><<<dim3(a.nsplit1, a.Hkv, a.B), kW * 64, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_stride == 0) return e;
     const dim3 grid((a.n_stride + kSnapColKeys - 1) / kSnapColKeys, a.Hkv, a.B);

@@ -1,0 +1,81 @@
+"""GPU parity of SnapKV selection with few observation rows per KV head (R = G * w <= 16),
+where the first pass keeps its scaled scores and the second pass reads them instead of K:
+scores within float32 rounding of the oracle, the selection bit-exact on the GPU's own scores,
+the same result through the path that re-reads K (unaligned workspace), and the NaN poisoning
+of a sequence whose block table holds an invalid block id."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.snapkv as osnap
+from kv_sparse_speculative_amd import kvss
+from kv_sparse_speculative_amd.synth import generate
+from kv_sparse_speculative_amd.workloads import WORKLOADS
+
+from _helpers import host
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("llama8b_ctx8k", 1, {"batch": 2}), ("llama8b_ctx8k", 3, {"batch": 2}),
+         ("llama8b_ctx8k", 4, {"batch": 3, "prompt": (37, 900)}),     # R = 16
+         ("llama8b_ctx8k", 5, {"batch": 2}),                          # R = 20: re-reads K
+         ("qwen32b_ragged", 3, {"batch": 3}),                         # G = 5: R = 15
+         ("llama8b_ctx32k", 2, {"batch": 1})]
+
+
+def _setup(name, w, kw):
+    torch.manual_seed(0)
+    ns = generate(WORKLOADS[name], device="cuda", parts=("attn",), **kw)
+    q_obs = ns.q_obs[:, :, -w:].contiguous()
+    P = ns.prompt_lens_np
+    kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.prompt_lens, int(P.max()))
+    return ns, q_obs, P, kv
+
+
+@pytest.mark.parametrize("name,w,kw", CASES, ids=[f"{c[0]}-w{c[1]}" for c in CASES])
+def test_small_window_matches_oracle(name, w, kw):
+    ns, q_obs, P, kv = _setup(name, w, kw)
+    wl = ns.workload
+    budget, pool = 64 + w, 5
+    sel, cnt, scores = kvss.snapkv_select(kv, q_obs, w, pool, budget, want_scores=True)
+    # the same call with a workspace 4 bytes past 16-byte alignment re-reads K in pass 2
+    d = kv.desc()
+    nbytes = kvss.lib().kvss_snapkv_workspace_bytes(__import__("ctypes").byref(d), wl.num_q_heads,
+                                                    w, budget)
+    big = torch.empty(nbytes + 16, dtype=torch.uint8, device="cuda")
+    sel2, cnt2, scores2 = kvss.snapkv_select(kv, q_obs, w, pool, budget, want_scores=True,
+                                             workspace=big[4:])
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(wl.head_dim)
+    ref_c = osnap.snapkv_scores(host(q_obs), host(ns.k_cache), ns.block_table_np, P, w, scale)
+    g_c, g_c2 = host(scores), host(scores2)
+    for b in range(ns.batch):
+        n = max(int(P[b]) - w, 0)
+        np.testing.assert_allclose(g_c[b, :, :n], ref_c[b, :, :n], rtol=1e-4, atol=1e-7)
+        np.testing.assert_allclose(g_c2[b, :, :n], g_c[b, :, :n], rtol=2e-5, atol=1e-8)
+    o_sel, o_cnt = osnap.select_from_scores(g_c.astype(np.float64), P, w, pool, budget)
+    np.testing.assert_array_equal(host(sel), o_sel)
+    np.testing.assert_array_equal(host(cnt), o_cnt)
+    o_sel2, _ = osnap.select_from_scores(g_c2.astype(np.float64), P, w, pool, budget)
+    np.testing.assert_array_equal(host(sel2), o_sel2)
+
+
+@pytest.mark.parametrize("w", [2, 5], ids=["stored", "reread"])
+def test_invalid_block_poisons_only_its_sequence(w):
+    ns, q_obs, P, kv = _setup("llama8b_ctx8k", w, {"batch": 3, "prompt": (600, 700)})
+    table = ns.block_table.clone()
+    table[1, 2] = ns.num_blocks + 7                   # out of range, inside sequence 1's prompt
+    kv_bad = kvss.PagedKV(ns.k_cache, ns.v_cache, table, ns.prompt_lens, int(P.max()))
+    _, _, scores = kvss.snapkv_select(kv_bad, q_obs, w, 5, 64 + w, want_scores=True)
+    torch.cuda.synchronize()
+    g = host(scores)
+    ref_c = osnap.snapkv_scores(host(q_obs), host(ns.k_cache), ns.block_table_np, P, w,
+                                1 / math.sqrt(ns.workload.head_dim))
+    n1 = int(P[1]) - w
+    assert np.isnan(g[1, :, :n1]).all()
+    for b in (0, 2):
+        n = int(P[b]) - w
+        np.testing.assert_allclose(g[b, :, :n], ref_c[b, :, :n], rtol=1e-4, atol=1e-7)
