@@ -164,6 +164,10 @@ KVSS_API int kvss_streaming_set(const int32_t* kv_lens, int batch, int num_kv_he
  *              (entries j >= P - w of a shorter prompt are left untouched).
  * The draft then attends sel_idx plus the dense tail [P - w, L).
  * Limits: 0 < w < budget, G * w <= 256, pool_kernel odd and >= 1.
+ * Workspace: kvss_snapkv_workspace_bytes. With bf16 and R = G * w <= 16 rows (4 R < head_dim)
+ * it includes the first pass's scaled scores, R floats per candidate, which the second pass
+ * reads instead of K; a workspace that is not 16-byte aligned makes the second pass re-read K
+ * (same selection, scores equal to float32 rounding).
  */
 KVSS_API size_t kvss_snapkv_workspace_bytes(const kvss_kv* kv, int num_q_heads, int w, int budget);
 KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads, int w, int pool_kernel,
