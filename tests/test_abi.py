@@ -179,3 +179,23 @@ def test_draft_sample_and_topk_validation():
     assert topk(wsb=16) == kvss.KVSS_EWORKSPACE
     assert lib.kvss_topk_workspace_bytes(ctypes.byref(d), 8, 16) > 0
 
+
+
+def test_snapkv_workspace_holds_stored_scores_for_few_rows():
+    """With bf16 and R = G * w <= 16 rows and 4 R < head_dim, the query adds the first pass's
+    scaled scores: R floats per candidate, the candidate count rounded up to 4. Nothing else in
+    the layout depends on head_dim, so the difference between head_dim 128 and 64 isolates it."""
+    L = kvss.lib()
+
+    def need(head_dim, w, dtype=kvss.KVSS_BF16):
+        d = _desc(batch=3, num_kv_heads=2, head_dim=head_dim, max_blocks=40, num_blocks=120,
+                  max_kv_len=601, dtype=dtype)
+        return L.kvss_snapkv_workspace_bytes(ctypes.byref(d), 8, w, w + 32)
+
+    # G = 4. w = 4: R = 16 is stored at head_dim 128 (64 < 128) but not at 64 (64 < 64 fails)
+    n4 = (601 - 4 + 3) // 4 * 4
+    extra = need(128, 4) - need(64, 4)
+    assert 3 * 2 * 16 * n4 * 4 <= extra < 3 * 2 * 16 * n4 * 4 + 4096, extra
+    assert need(128, 1) == need(64, 1)              # R = 4: stored at both head sizes
+    assert need(128, 5) == need(64, 5)              # R = 20: never stored
+    assert need(128, 4, kvss.KVSS_F32) == need(64, 4, kvss.KVSS_F32)   # fp32: never stored
