@@ -96,3 +96,24 @@ def test_draft_sample_scalar_path(vocab, shift, temp):
     np.testing.assert_allclose(host(st)[:, 1], ref_s, rtol=1e-4)
     bad = [b for b in range(9) if g[b] != ref[b] and not _near_tie(z[b], temp, seed, offset, b, step)]
     assert not bad, bad
+
+
+@pytest.mark.parametrize("temp", [1e-3, 1e4], ids=["cold", "hot"])
+def test_draft_sample_extreme_temperatures(temp):
+    """A cold temperature concentrates the law on the argmax (z/t spans ~1e4 in log space); a hot
+    one makes it nearly uniform. Tokens match the oracle except at flagged near-ties, and the
+    row statistics stay finite."""
+    ns = generate(WORKLOADS["llama8b_ctx8k"], device="cuda", batch=16, parts=("accept",), vocab=5000)
+    logits = ns.draft_logits[:, 0].contiguous()
+    seed, offset, step = 99, 1, 0
+    tok, st = kvss.draft_sample(logits, temp, seed, offset, step, want_stats=True)
+    torch.cuda.synchronize()
+    z = host(logits).astype(np.float64)
+    ref = oacc.draft_sample(z, temp, seed, offset, step)
+    g = host(tok)
+    assert np.isfinite(host(st)).all()
+    y = z / temp
+    ref_s = np.exp(y - y.max(axis=1, keepdims=True)).sum(axis=1)
+    np.testing.assert_allclose(host(st)[:, 1], ref_s, rtol=1e-4)
+    bad = [b for b in range(16) if g[b] != ref[b] and not _near_tie(z[b], temp, seed, offset, b, step)]
+    assert not bad, bad
