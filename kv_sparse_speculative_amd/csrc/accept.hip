@@ -204,11 +204,15 @@ __global__ __launch_bounds__(64) void accept_decide_kernel(AcceptArgs a, const P
         if (greedy) {
             ok = (int)st[n][3] == x;
         } else {
-            const float p = __expf(st[n][2] - st[n][0]) / st[n][1];
-            const float q = __expf(st[gamma + 1 + n][2] - st[gamma + 1 + n][0]) / st[gamma + 1 + n][1];
+            // p(x) / q(x) as one exp2 of a difference of logs: at a low temperature p(x) and
+            // q(x) alone can underflow float while their ratio is ordinary.
+            const float* t = st[n];
+            const float* d = st[gamma + 1 + n];
+            const float lp = (t[2] - t[0]) * kLog2e - __log2f(t[1]);
+            const float lq = (d[2] - d[0]) * kLog2e - __log2f(d[1]);
             uint32_t c0 = 0, c1 = (uint32_t)n, c2 = (uint32_t)b, c3 = (uint32_t)a.offset;
             philox4x32_10(c0, c1, c2, c3, k0, k1);
-            ok = (x >= 0 && x < V) && philox_uniform(c0) < p / q;
+            ok = (x >= 0 && x < V) && philox_uniform(c0) < __builtin_amdgcn_exp2f(lp - lq);
         }
         if (!ok) break;
         out[n] = x;

@@ -188,7 +188,7 @@ def _stats_decisions(st, tokens, gamma, temp, seed, offset, b):
 @pytest.mark.parametrize("name,batch,vocab", [("tiny_fp32", 2, None), ("llama8b_ctx8k", 6, None),
                                               ("qwen32b_ragged", 4, None),
                                               ("llama8b_ctx32k", 16, 1001)])
-@pytest.mark.parametrize("temp", [0.0, 1.0, 0.7])
+@pytest.mark.parametrize("temp", [0.0, 1.0, 0.7, 0.05, 20.0])
 def test_accept_matches_oracle(name, batch, vocab, temp):
     ns = generate(WORKLOADS[name], device="cuda", batch=batch, parts=("accept",), vocab=vocab)
     seed, offset = 0x5EED0000 + batch, 17
