@@ -48,7 +48,8 @@ def exponential_race(weights, u):
     u = np.asarray(u, dtype=np.float64)
     live = weights > 0
     keys = np.full(weights.shape, np.inf)
-    keys[live] = -np.log(u[live]) / weights[live]
+    with np.errstate(over="ignore"):      # a subnormal weight gives key +inf: it cannot win
+        keys[live] = -np.log(u[live]) / weights[live]
     return argmax_lowest(-keys)
 
 
