@@ -44,7 +44,8 @@ long ceil_div(long a, long b) { return (a + b - 1) / b; }
 constexpr long kTargetWorkgroups = 1024;
 // Draft launches: one round of resident workgroups (two per CU).
 constexpr long kDraftTargetWorkgroups = 2 * 256;
-// The SnapKV row-statistics pass fits three workgroups per CU: aim at four full rounds.
+// The SnapKV row-statistics pass keeps two (eight row tiles) or three (fewer) workgroups per
+// CU resident: 3072 workgroups are whole rounds either way (six or four).
 constexpr long kSnapTargetWorkgroups = 3 * 256 * 4;
 constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes per round
 constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
