@@ -26,9 +26,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "KV-attn HBM GB/s (% peak) + verify/draft tokens/s, B=64 S=32000, 1 GPU"
-VERIFY_KERNEL = "attn_mfma_kernel<128, false, 2>"
 KERNEL_SOURCE = os.path.join(ROOT, "kv_sparse_speculative_amd", "csrc", "attn_mfma.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "verify_attn_llama8b_ctx32k_traffic.md")
 COPY_BYTES = 1 << 30          # plain copy used to calibrate the HBM byte counters
 
 
@@ -47,13 +45,36 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per verify launch from the committed counter summary, if it was taken on the
-    current kernel source; otherwise None."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def traffic_summary_path(workload):
+    """The committed counter summary of the verify kernel on one workload."""
+    return os.path.join(ROOT, "profiles", f"verify_attn_{workload}_traffic.md")
+
+
+def verify_kernel_name(wl):
+    """The verify kernel instance a workload launches (one 16-row tile up to 16 query rows per
+    KV head, else two)."""
+    rows = wl.group * (wl.gamma + 1)
+    if wl.dtype != "bf16":
+        return f"attn_simple_kernel<{wl.head_dim}, false>"
+    return f"attn_mfma_kernel<{wl.head_dim}, false, {1 if rows <= 16 else 2}>"
+
+
+def verify_algorithmic_bytes(wl):
+    """Algorithmic bytes of one verify call on a workload (the same definition as the timed
+    run's: every K and V row once, Q, the fp32 output and LSE)."""
+    from kv_sparse_speculative_amd.synth import prompt_lengths
+    P = prompt_lengths(wl)
+    return algorithmic_bytes(wl, P, wl.gamma + 1, 16, 496, wl.vocab)["verify"]
+
+
+def committed_traffic(workload):
+    """HBM bytes per verify launch from the committed counter summary of this workload, if one
+    exists and was taken on the current kernel source; otherwise None."""
+    path = traffic_summary_path(workload)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_SUMMARY):
+    for line in open(path):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
@@ -74,20 +95,28 @@ def _read_csv_rows(directory, suffix):
     return rows
 
 
-def summarize_pmc(fetch_dir, write_dir, out_path, command):
+def summarize_pmc(fetch_dir, write_dir, out_path, command, wl):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the verify kernel and of the calibration
-    copy -> profiles summary with the copy-scaled HBM bytes per verify launch."""
+    copy -> profiles summary with the copy-scaled HBM bytes per verify launch on workload wl."""
+    kernel = verify_kernel_name(wl)
+    algo = verify_algorithmic_bytes(wl)
     def per_kernel(directory, counter):
         vals = {}
         for r in _read_csv_rows(directory, "counter_collection.csv"):
             if r.get("Counter_Name") != counter:
                 continue
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            vals.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
         return vals
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
-    pick = lambda d, key: next((v for k, v in d.items() if key in k), None)
-    vf, vw = pick(fetch, VERIFY_KERNEL), pick(write, VERIFY_KERNEL)
+    pick = lambda d, key: next((v for k, v in d.items() if key in k), [])
+    # The verify launches are the kernel's dispatches with the grid of its largest read (a T = 1
+    # decode over the compact draft cache can run the same kernel instance on a smaller grid).
+    grid = max(pick(fetch, kernel), key=lambda gv: gv[1])[0]
+    vf = [v for g, v in pick(fetch, kernel) if g == grid]
+    vw = [v for g, v in pick(write, kernel) if g == grid]
+    fetch = {k: [v for _, v in gv] for k, gv in fetch.items()}
+    write = {k: [v for _, v in gv] for k, gv in write.items()}
     # calibration copy: torch's device-to-device copy of COPY_BYTES runs as the runtime's blit
     # kernel; its largest dispatches are the 1 GiB copies
     cf = [v for k, v in fetch.items() if "copyBuffer" in k]
@@ -101,21 +130,23 @@ def summarize_pmc(fetch_dir, write_dir, out_path, command):
     write_b = mean(vw) * 1024 * w_scale
     total = int(fetch_b + write_b)
     lines = [
-        "# Verify attention (Llama-3.1-8B-shaped layer, B=64, context 32000, gamma 4): HBM traffic",
+        f"# Verify attention on `{wl.name}` (batch {wl.batch}, {wl.num_q_heads} / {wl.num_kv_heads} "
+        f"heads, head_dim {wl.head_dim}, prompts {wl.prompt[0]}-{wl.prompt[1]}, gamma {wl.gamma}): "
+        "HBM traffic",
         "",
         "Counter runs (each counter in its own run), then this summary:",
         "",
         *[f"    {c}" for c in command],
         "",
-        f"- kernel: `{VERIFY_KERNEL}`",
+        f"- kernel: `{kernel}`",
         f"- kernel source sha256/16: `{source_digest()}`",
         f"- FETCH_SIZE per dispatch (KiB, mean of {len(vf)}): {mean(vf):.1f}",
         f"- WRITE_SIZE per dispatch (KiB, mean of {len(vw)}): {mean(vw):.1f}",
         f"- calibration copy of {COPY_BYTES} B: FETCH_SIZE {cfk:.1f} KiB, WRITE_SIZE {cwk:.1f} KiB",
         f"- scale factors (bytes / counter bytes): fetch {f_scale:.4f}, write {w_scale:.4f}",
         f"- HBM bytes per launch: {total}",
-        f"- algorithmic bytes per launch: 8397824000",
-        f"- traffic / algorithmic: {total / 8397824000:.4f}",
+        f"- algorithmic bytes per launch: {algo}",
+        f"- traffic / algorithmic: {total / algo:.4f}",
     ]
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -404,7 +435,8 @@ def main():
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.command)
+        from kv_sparse_speculative_amd.workloads import HEADLINE, WORKLOADS
+        summarize_pmc(*args.summarize_pmc, args.command, WORKLOADS[args.workload or HEADLINE])
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats, args.title, args.command)
@@ -563,7 +595,7 @@ def main():
                    "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": D,
                    "snapkv_budget": budget, "streaming": [sink, window], "vocab": ns.vocab},
         "roofline": {"bound": "hbm", "achieved": v["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": v["frac_peak"], "traffic": committed_traffic(),
+                     "frac": v["frac_peak"], "traffic": committed_traffic(wl.name),
                      "kernel": "verify_attn_full"},
         "calls": detail,
         "stream_read_GB_per_s": round(stream_gbs, 1),
