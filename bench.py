@@ -152,8 +152,31 @@ def summarize_pmc(fetch_dir, write_dir, out_path, command, wl):
     print("\n".join(lines))
 
 
-def summarize_stats(stats_dir, out_path, title, command):
-    """rocprofv3 --stats kernel table (kvss kernels) -> profiles summary."""
+def verify_dispatches(stats_dir, wl, warmup):
+    """Durations (us) of the verify call's kernels in the timed steps, from the kernel trace: the
+    verify kernel instance's dispatches with the grid of its longest one (a T = 1 decode over
+    the compact draft cache can run the same instance on a smaller grid), in launch order, less
+    the first `warmup`; and the split-merge dispatches that follow each of them."""
+    rows = _read_csv_rows(stats_dir, "kernel_trace.csv")
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    name = verify_kernel_name(wl)
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    mine = [r for r in rows if name in r["Kernel_Name"]]
+    if not mine:
+        return [], []
+    grid = max(mine, key=dur)["Grid_Size_X"]
+    attn, merge = [], []
+    for i, r in enumerate(rows):
+        if name in r["Kernel_Name"] and r["Grid_Size_X"] == grid:
+            nxt = rows[i + 1] if i + 1 < len(rows) else None
+            attn.append(dur(r))
+            merge.append(dur(nxt) if nxt is not None and "merge_kernel" in nxt["Kernel_Name"] else 0.0)
+    return attn[warmup:], merge[warmup:]
+
+
+def summarize_stats(stats_dir, out_path, title, command, wl=None, warmup=3):
+    """rocprofv3 --stats kernel table (kvss kernels) -> profiles summary; with a workload, also
+    the verify call's kernel times over the timed steps (the span bench.py's events measure)."""
     rows = _read_csv_rows(stats_dir, "kernel_stats.csv")
     lines = [f"# {title}", "", "Command:", "", *[f"    {c}" for c in command], "",
              "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
@@ -163,6 +186,18 @@ def summarize_stats(stats_dir, out_path, title, command):
         name = r["Name"].replace("kvss::(anonymous namespace)::", "").replace("(kvss::", "(")
         lines.append(f"| `{name[:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    if wl is not None:
+        attn, merge = verify_dispatches(stats_dir, wl, warmup)
+        if attn:
+            mean = lambda v: sum(v) / len(v)
+            algo = verify_algorithmic_bytes(wl)
+            total = mean(attn) + mean(merge)
+            lines += ["", f"Verify calls in the timed steps ({len(attn)} calls after {warmup} warm-up "
+                      f"calls; `{verify_kernel_name(wl)}` followed by `merge_kernel`):", "",
+                      f"- attention kernel average: {mean(attn):.2f} us (min {min(attn):.2f}, max {max(attn):.2f})",
+                      f"- split merge average: {mean(merge):.2f} us",
+                      f"- call (attention + merge): {total:.2f} us, "
+                      f"{algo / (total * 1e-6) / 1e9:.1f} GB/s of {algo} algorithmic bytes"]
     open(out_path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -439,7 +474,9 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.command, WORKLOADS[args.workload or HEADLINE])
         return
     if args.summarize_stats:
-        summarize_stats(*args.summarize_stats, args.title, args.command)
+        from kv_sparse_speculative_amd.workloads import HEADLINE, WORKLOADS
+        summarize_stats(*args.summarize_stats, args.title, args.command,
+                        WORKLOADS[args.workload or HEADLINE], args.warmup)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path is not sharded across GPUs (run with --gpus 1)",
