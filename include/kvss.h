@@ -306,6 +306,21 @@ KVSS_API int kvss_draft_cache_build(const kvss_kv* src, const int32_t* sel_idx,
  */
 KVSS_API int kvss_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * kvss_philox4x32_10 -- the generator behind the draws of spec_accept and draft_sample,
+ * evaluated on caller-given counters (MagicDec Section 3.1: speculative sampling consumes
+ * uniform draws; the paper leaves their source open, and this library takes Philox4x32-10 of
+ * Salmon et al., SC'11, with the counter layouts documented above). A caller can replay any
+ * draw the library made, e.g. u_i of spec_accept is word 0 of counter (0, i, b, offset low
+ * 32 bits) under seed `seed`.
+ *   counters  uint32 [n, 4] (device, 16-byte aligned): counter words (c0, c1, c2, c3)
+ *   seed      the key is (seed low 32 bits, seed high 32 bits)
+ *   out       uint32 [n, 4] (device, 16-byte aligned), written: the four output words
+ * n == 0 is a no-op; n < 0 or a NULL / misaligned pointer is KVSS_EINVAL.
+ */
+KVSS_API int kvss_philox4x32_10(const uint32_t* counters, int64_t n, uint64_t seed, uint32_t* out,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvss.so")
 SOURCES = ["api.hip", "attn_mfma.hip", "attn_simple.hip", "merge.hip", "snapkv.hip", "snapkv_mfma.hip",
-           "accept.hip", "streaming.hip", "stream.hip", "cache.hip", "sample.hip"]
+           "accept.hip", "streaming.hip", "stream.hip", "cache.hip", "sample.hip", "philox.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",

@@ -581,4 +581,17 @@ int kvss_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream
                       "stream read launch");
 }
 
+int kvss_philox4x32_10(const uint32_t* counters, int64_t n, uint64_t seed, uint32_t* out,
+                       void* stream) {
+    if (n < 0) return fail(KVSS_EINVAL, "n must be >= 0 (got %lld)", (long long)n);
+    if (n == 0) return ok();
+    if (!counters || !out) return fail(KVSS_EINVAL, "counters and out must be non-NULL");
+    if (!aligned16(counters) || !aligned16(out))
+        return fail(KVSS_EINVAL, "counters and out must be 16-byte aligned");
+    if (n > (int64_t)0xffffffff * 256)
+        return fail(KVSS_EUNSUPPORTED, "n = %lld exceeds the launch limit", (long long)n);
+    return hip_status(kvss::launch_philox(counters, n, seed, out, static_cast<hipStream_t>(stream)),
+                      "philox launch");
+}
+
 }  // extern "C"

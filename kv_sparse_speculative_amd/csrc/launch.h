@@ -140,5 +140,7 @@ size_t sample_workspace_bytes(int B, int V);
 hipError_t launch_sample(const SampleArgs& a, void* workspace, hipStream_t s);
 
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_philox(const uint32_t* counters, int64_t n, uint64_t seed, uint32_t* out,
+                         hipStream_t s);
 
 }  // namespace kvss

@@ -63,6 +63,7 @@ _SIGNATURES = {
     "draft_sample": (_I, [_P, _I, _I, _F, _U64, _U64, _I, _P, _P, _P, _Z, _P]),
     "draft_attn_topk": (_I, [_KV, _P, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P]),
     "kvss_draft_cache_build": (_I, [_KV, _P, _P, _I, _P, _I, _KV, _P, _P]),
+    "kvss_philox4x32_10": (_I, [_P, ctypes.c_int64, _U64, _P, _P]),
 }
 
 _lib = None
@@ -268,6 +269,20 @@ def kvss_stream_read(buf, sink, stream=None):
     _need(sink, "sink")
     _check(lib().kvss_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
                                   _stream(stream)))
+
+
+def kvss_philox4x32_10(counters, seed, out=None, stream=None):
+    """The library's Philox4x32-10 on counters int32/uint32-bit words [n, 4] (device, stored as
+    torch.int32); returns the output words [n, 4] as torch.int32 bit patterns."""
+    _need(counters, "counters", torch.int32)
+    if counters.dim() != 2 or counters.shape[1] != 4:
+        raise ValueError("counters must be [n, 4]")
+    if out is None:
+        out = torch.empty_like(counters)
+    _need(out, "out", torch.int32)
+    _check(lib().kvss_philox4x32_10(counters.data_ptr(), counters.shape[0], int(seed) & (2**64 - 1),
+                                    out.data_ptr(), _stream(stream)))
+    return out
 
 
 def kvss_kv_append(kv, k_new, v_new, start, stream=None):

@@ -199,3 +199,12 @@ def test_snapkv_workspace_holds_stored_scores_for_few_rows():
     assert need(128, 1) == need(64, 1)              # R = 4: stored at both head sizes
     assert need(128, 5) == need(64, 5)              # R = 20: never stored
     assert need(128, 4, kvss.KVSS_F32) == need(64, 4, kvss.KVSS_F32)   # fp32: never stored
+
+
+def test_philox_validation():
+    L = kvss.lib()
+    assert L.kvss_philox4x32_10(FAKE, -1, 0, FAKE, None) == kvss.KVSS_EINVAL
+    assert L.kvss_philox4x32_10(None, 4, 0, FAKE, None) == kvss.KVSS_EINVAL
+    assert L.kvss_philox4x32_10(FAKE, 4, 0, None, None) == kvss.KVSS_EINVAL
+    assert L.kvss_philox4x32_10(FAKE + 4, 4, 0, FAKE, None) == kvss.KVSS_EINVAL    # misaligned
+    assert L.kvss_philox4x32_10(None, 0, 0, None, None) == kvss.KVSS_OK
