@@ -27,6 +27,7 @@
 //       MFMA operand, keep plain loads (routing K through LDS as well measured slower).
 // Waves merge (max, sum, O) through LDS; with one split the workgroup writes the final
 // normalised output, otherwise (m, l, o) partials that the merge kernel combines.
+// Over the full cache, sequences are taken longest first (see the kernel's prologue).
 
 #include "common.h"
 #include "launch.h"
@@ -36,6 +37,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr unsigned kInvalidRow = 0xffffffffu;
+// Largest batch whose workgroups order themselves longest-first (each ranks every sequence:
+// O(B^2 / 64) work per workgroup).
+constexpr int kLongestFirstMaxBatch = 256;
 
 template <int D, int NRT>
 struct MfmaCfg {
@@ -59,6 +63,52 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
     return r;
 }
 
+// Workgroups are dispatched in grid order, so the z-th row of the grid taking the sequence of
+// rank z in decreasing length (ties: lower index) starts the longest sequences first and ends a
+// ragged batch with short ones instead of a long tail. Every wave computes the same answer
+// from one vector load of the lengths per 64 sequences, with no LDS or barrier; a batch of
+// equal lengths keeps z (the wave-uniform min == max test) and skips the ranking.
+__device__ __forceinline__ int longest_first(const AttnArgs& a, int z, int lane) {
+    constexpr int kChunks = kLongestFirstMaxBatch / 64;
+    int len[kChunks];
+    int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int j = c * 64 + lane;
+        len[c] = -1;
+        if (c * 64 < a.B && j < a.B) {
+            len[c] = max(min(a.kv_lens[j], a.max_kv_len), 0);
+            lo = min(lo, len[c]);
+            hi = max(hi, len[c]);
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        lo = min(lo, __shfl_xor(lo, o));
+        hi = max(hi, __shfl_xor(hi, o));
+    }
+    if (__builtin_amdgcn_readfirstlane(lo) == __builtin_amdgcn_readfirstlane(hi)) return z;
+    int found = -1;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        if (c * 64 >= a.B) break;
+        const int j = c * 64 + lane;
+        int rank = 0;
+#pragma unroll
+        for (int c2 = 0; c2 < kChunks; ++c2) {
+            if (c2 * 64 >= a.B) break;
+            const int n = min(64, a.B - c2 * 64);
+            for (int t = 0; t < n; ++t) {
+                const int Li = __builtin_amdgcn_readlane(len[c2], t);
+                rank += (Li > len[c] || (Li == len[c] && c2 * 64 + t < j)) ? 1 : 0;
+            }
+        }
+        if (j < a.B && rank == z) found = j;
+    }
+    const unsigned long long hit = __ballot(found >= 0);       // exactly one lane
+    return hit != 0ull ? __builtin_amdgcn_readlane(found, __ffsll((long long)hit) - 1) : z;
+}
+
 // With one row tile the kernel fits two workgroups per CU (<= 256 registers per lane), so a
 // draft launch of B * Hkv workgroups is resident in a single round.
 template <int D, bool GATHER, int NRT>
@@ -74,8 +124,14 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m16 = lane & 15, q4 = lane >> 4;
-    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x, g = blockIdx.y;
     if (tid == 0) s_bad = 0;
+    // Sequence of this workgroup: over the full cache (work proportional to the length) a
+    // ragged batch is taken longest first (see longest_first).
+    int b = blockIdx.z;
+    if constexpr (!GATHER) {
+        if (a.B > 1 && a.B <= kLongestFirstMaxBatch) b = longest_first(a, blockIdx.z, lane);
+    }
 
     const int L = max(min(a.kv_lens[b], a.max_kv_len), 0);
     int n_list = 0, lo = 0;

@@ -24,7 +24,8 @@ def lse_err(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     both_inf = np.isneginf(got) & np.isneginf(ref)
-    d = np.where(both_inf, 0.0, np.abs(got - ref) / np.maximum(1.0, np.abs(ref)))
+    with np.errstate(invalid="ignore"):          # -inf - (-inf) is masked out just below
+        d = np.where(both_inf, 0.0, np.abs(got - ref) / np.maximum(1.0, np.abs(ref)))
     return float(d.max()) if d.size else 0.0
 
 
