@@ -59,14 +59,15 @@ struct Plan {
 };
 
 // Split a virtual key range of up to max_total keys per (sequence, KV head) so that the
-// launch offers about kTargetWorkgroups workgroups, each doing at least eight rounds (a
-// shorter split would not pay for the extra merge launch and partial traffic).
+// launch offers about `target` workgroups, each doing at least eight rounds (a shorter split
+// would not pay for the extra merge launch and partial traffic); a range shorter than
+// `unsplit_below` keys is not split at all.
 Plan plan_splits(long pairs, long max_total, int unit, long max_len = 1L << 30,
-                 long target = kTargetWorkgroups) {
+                 long target = kTargetWorkgroups, long unsplit_below = 0) {
     Plan p{1, unit};
     if (max_total <= 0 || pairs <= 0) return p;
     const long want = ceil_div(target, pairs);
-    const long useful = ceil_div(max_total, 8L * unit);
+    const long useful = max_total < unsplit_below ? 1 : ceil_div(max_total, 8L * unit);
     long ns = want < useful ? want : useful;
     if (ns < 1) ns = 1;
     if (ceil_div(max_total, ns) > max_len) ns = ceil_div(max_total, max_len);
@@ -122,9 +123,16 @@ kvss::AttnArgs attn_common(const kvss_kv* kv) {
 
 float scale_log2(float scale) { return (float)((double)scale * 1.4426950408889634); }
 
+// bf16 verify: contexts under 16k keys are not split. Measured on the Llama-shaped layer (B
+// 32-128, gamma 3-4): an 8k context runs fastest unsplit (no merge launch; whole-sequence
+// workgroups already saturate HBM), while longer contexts gain from the regular plan.
+constexpr long kVerifyUnsplitBelow = 16384;
+
 Plan verify_plan(const kvss_kv* kv) {
-    return plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len,
-                       kv->dtype == KVSS_BF16 ? kMfmaUnit : kSimpleUnit);
+    return kv->dtype == KVSS_BF16
+               ? plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kMfmaUnit,
+                             1L << 30, kTargetWorkgroups, kVerifyUnsplitBelow)
+               : plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kSimpleUnit);
 }
 
 size_t partial_bytes(long rows, const Plan& p, int D) {

@@ -240,8 +240,9 @@ def test_verify_is_deterministic_and_layout_free():
 
 
 def test_verify_independent_of_split_plan():
-    """A batch of one and the same sequence inside a larger batch get different split plans."""
-    ns = _inputs("llama8b_ctx8k", {"batch": 16})
+    """A batch of one and the same sequence inside a larger batch get different split plans:
+    at a 20000-key context a single sequence is split 20 ways, a batch of 16 eight ways."""
+    ns = _inputs("llama8b_ctx32k", {"batch": 16, "prompt": (20000, 20000)})
     kv = _kv(ns, ns.kv_lens_verify, int(ns.prompt_lens_np.max()) + ns.T)
     full, _ = kvss.verify_attn_full(kv, ns.q_verify)
     one = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table[:1].contiguous(),
