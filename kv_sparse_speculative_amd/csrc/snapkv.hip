@@ -189,13 +189,30 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     const float* c = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
     unsigned* pl = reinterpret_cast<unsigned*>(a.pooled + ((size_t)b * a.Hkv + g) * a.n_stride);
     const int r = a.pool / 2;
-    for (int j = tid; j < n; j += 1024) {
-        float m = c[j];
-        for (int d = 1; d <= r; ++d) {
-            if (j - d >= 0) m = fmaxf(m, c[j - d]);
-            if (j + d < n) m = fmaxf(m, c[j + d]);
+    // Every loop below issues a batch of independent loads before using any (the pooled array
+    // is re-read from L2 on every pass; one load at a time would wait out its latency each).
+    constexpr int kBatch = 8;
+    for (int j0 = tid; j0 < n; j0 += kBatch * 1024) {
+        float m[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int j = j0 + q * 1024;
+            m[q] = j < n ? c[j] : 0.f;
         }
-        pl[j] = __float_as_uint(m);
+        for (int d = 1; d <= r; ++d) {
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int j = j0 + q * 1024;
+                const float lft = (j < n && j - d >= 0) ? c[j - d] : kNegInf;
+                const float rgt = (j + d < n) ? c[j + d] : kNegInf;
+                m[q] = fmaxf(m[q], fmaxf(lft, rgt));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int j = j0 + q * 1024;
+            if (j < n) pl[j] = __float_as_uint(m[q]);
+        }
     }
     __syncthreads();
 
@@ -210,19 +227,30 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
         const int shift = 24 - 8 * pass;
         for (int t = tid; t < 256; t += 1024) hist[t] = 0;
         __syncthreads();
-        for (int j = tid; j < n_pad; j += 1024) {
-            const unsigned u = j < n ? pl[j] : 0u;
-            const bool match = j < n && (u & mask) == prefix;
-            const unsigned bin = (u >> shift) & 255u;
-            unsigned long long peers = __ballot(match);
+        for (int j0 = tid; j0 < n_pad; j0 += kBatch * 1024) {
+            unsigned uu[kBatch];
 #pragma unroll
-            for (int bit = 0; bit < 8; ++bit) {
-                const bool set = (bin >> bit) & 1u;
-                const unsigned long long m = __ballot(set);
-                peers &= set ? m : ~m;
+            for (int q = 0; q < kBatch; ++q) {
+                const int j = j0 + q * 1024;
+                uu[q] = j < n ? pl[j] : 0u;
             }
-            if (match && __ffsll((long long)peers) - 1 == lane)
-                atomicAdd(&hist[bin], (unsigned)__popcll(peers));
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int j = j0 + q * 1024;
+                if (j0 - tid + q * 1024 >= n_pad) break;      // uniform: whole 1024-blocks
+                const unsigned u = uu[q];
+                const bool match = j < n && (u & mask) == prefix;
+                const unsigned bin = (u >> shift) & 255u;
+                unsigned long long peers = __ballot(match);
+#pragma unroll
+                for (int bit = 0; bit < 8; ++bit) {
+                    const bool set = (bin >> bit) & 1u;
+                    const unsigned long long m = __ballot(set);
+                    peers &= set ? m : ~m;
+                }
+                if (match && __ffsll((long long)peers) - 1 == lane)
+                    atomicAdd(&hist[bin], (unsigned)__popcll(peers));
+            }
         }
         __syncthreads();
         // Find the bin where the count from the top first reaches `remaining`.
@@ -244,19 +272,28 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     const int chunk = (n + 1023) / 1024;
     const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
     int gt = 0, eq = 0;
-    for (int j = lo; j < hi; ++j) {
-        const unsigned u = pl[j];
-        gt += u > thr;
-        eq += u == thr;
+    for (int j = lo; j < hi; j += kBatch) {
+        unsigned uu[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) uu[q] = j + q < hi ? pl[j + q] : 0u;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            if (j + q < hi) { gt += uu[q] > thr; eq += uu[q] == thr; }
     }
     int tot;
     const int eq_before = block_scan_1024(eq, sh, tot);
     int take = min(max((int)remaining - eq_before, 0), eq);
     int pos = block_scan_1024(gt + take, sh, tot);
-    for (int j = lo; j < hi && pos < k; ++j) {
-        const unsigned u = pl[j];
-        if (u > thr) out[pos++] = j;
-        else if (u == thr && take > 0) { out[pos++] = j; --take; }
+    for (int j = lo; j < hi && pos < k; j += kBatch) {
+        unsigned uu[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) uu[q] = j + q < hi ? pl[j + q] : 0u;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            if (j + q >= hi || pos >= k) break;
+            if (uu[q] > thr) out[pos++] = j + q;
+            else if (uu[q] == thr && take > 0) { out[pos++] = j + q; --take; }
+        }
     }
 }
 
