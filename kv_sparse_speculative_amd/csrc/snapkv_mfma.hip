@@ -138,8 +138,11 @@ __device__ __forceinline__ void read_q(const uint4* qs, int t, int lane, uint4 (
 // NT row tiles (16 rows each, rows past R are zero queries whose statistics are not written).
 // STORE (one row tile only): also write each row's scaled scores of the candidate keys
 // j < P - w to a.xs (NaN for a key whose block id is invalid), for the stored second pass.
+// Sixteen row tiles would take 259 registers (one wave per SIMD); bounding them to two
+// workgroups per CU costs two spilled registers and runs the pass ~10% faster (256 rows at a
+// 100k context: SnapKV select 2.98-3.08 -> 2.71 ms, same selection).
 template <int D, int NT, bool STORE>
-__global__ __launch_bounds__(kW * 64) void snap_rowstats_mfma(SnapArgs a) {
+__global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(SnapArgs a) {
     static_assert(!STORE || NT == 1, "stored scores use one row tile");
     constexpr int KS = D / 32;
     constexpr int QS = NT * KS * 64 * 16;                  // queries in MFMA operand order
