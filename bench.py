@@ -102,21 +102,22 @@ def summarize_pmc(fetch_dir, write_dir, out_path, command, wl):
     algo = verify_algorithmic_bytes(wl)
     def per_kernel(directory, counter):
         vals = {}
-        for r in _read_csv_rows(directory, "counter_collection.csv"):
-            if r.get("Counter_Name") != counter:
-                continue
-            vals.setdefault(r["Kernel_Name"], []).append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+        rows = [r for r in _read_csv_rows(directory, "counter_collection.csv")
+                if r.get("Counter_Name") == counter]
+        for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
     pick = lambda d, key: next((v for k, v in d.items() if key in k), [])
-    # The verify launches are the kernel's dispatches with the grid of its largest read (a T = 1
-    # decode over the compact draft cache can run the same kernel instance on a smaller grid).
-    grid = max(pick(fetch, kernel), key=lambda gv: gv[1])[0]
-    vf = [v for g, v in pick(fetch, kernel) if g == grid]
-    vw = [v for g, v in pick(write, kernel) if g == grid]
-    fetch = {k: [v for _, v in gv] for k, gv in fetch.items()}
-    write = {k: [v for _, v in gv] for k, gv in write.items()}
+    # The verify launches are the dispatches of the verify kernel instance that read at least
+    # half its largest read (a T = 1 decode over the compact draft cache can run the same
+    # instance); both runs execute the same program, so the write run's dispatches of that
+    # instance are matched by launch order.
+    kf, kw = pick(fetch, kernel), pick(write, kernel)
+    idx = [i for i, v in enumerate(kf) if v >= 0.5 * max(kf)]
+    vf = [kf[i] for i in idx]
+    vw = [kw[i] for i in idx if i < len(kw)]
     # calibration copy: torch's device-to-device copy of COPY_BYTES runs as the runtime's blit
     # kernel; its largest dispatches are the 1 GiB copies
     cf = [v for k, v in fetch.items() if "copyBuffer" in k]
@@ -154,9 +155,9 @@ def summarize_pmc(fetch_dir, write_dir, out_path, command, wl):
 
 def verify_dispatches(stats_dir, wl, warmup):
     """Durations (us) of the verify call's kernels in the timed steps, from the kernel trace: the
-    verify kernel instance's dispatches with the grid of its longest one (a T = 1 decode over
-    the compact draft cache can run the same instance on a smaller grid), in launch order, less
-    the first `warmup`; and the split-merge dispatches that follow each of them."""
+    verify kernel instance's dispatches that last at least half its longest one (a T = 1 decode
+    over the compact draft cache can run the same instance), in launch order, less the first
+    `warmup`; and the split-merge dispatches that follow each of them."""
     rows = _read_csv_rows(stats_dir, "kernel_trace.csv")
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
     name = verify_kernel_name(wl)
@@ -164,10 +165,10 @@ def verify_dispatches(stats_dir, wl, warmup):
     mine = [r for r in rows if name in r["Kernel_Name"]]
     if not mine:
         return [], []
-    grid = max(mine, key=dur)["Grid_Size_X"]
+    longest = max(dur(r) for r in mine)
     attn, merge = [], []
     for i, r in enumerate(rows):
-        if name in r["Kernel_Name"] and r["Grid_Size_X"] == grid:
+        if name in r["Kernel_Name"] and dur(r) >= 0.5 * longest:
             nxt = rows[i + 1] if i + 1 < len(rows) else None
             attn.append(dur(r))
             merge.append(dur(nxt) if nxt is not None and "merge_kernel" in nxt["Kernel_Name"] else 0.0)
