@@ -32,14 +32,13 @@ COPY_BYTES = 1 << 30          # plain copy used to calibrate the HBM byte counte
 
 def source_digest():
     """Digest of what decides the verify kernel's code and launch: its source, the headers it
-    includes, the entry point that plans it, and the compiler flags."""
+    includes, the planner that splits its key ranges, and the compiler flags."""
     import hashlib
     from kv_sparse_speculative_amd import build as kbuild
     h = hashlib.sha256()
     csrc = os.path.dirname(KERNEL_SOURCE)
-    # the kernel, the headers it includes, and the entry point that plans its launch
     for path in (KERNEL_SOURCE, os.path.join(csrc, "common.h"), os.path.join(csrc, "launch.h"),
-                 os.path.join(csrc, "api.hip")):
+                 os.path.join(csrc, "plan.h")):
         h.update(open(path, "rb").read())
     h.update(" ".join(kbuild.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]

@@ -316,7 +316,8 @@ KVSS_API int kvss_stream_read(const void* src, size_t bytes, uint32_t* sink, voi
  *   counters  uint32 [n, 4] (device, 16-byte aligned): counter words (c0, c1, c2, c3)
  *   seed      the key is (seed low 32 bits, seed high 32 bits)
  *   out       uint32 [n, 4] (device, 16-byte aligned), written: the four output words
- * n == 0 is a no-op; n < 0 or a NULL / misaligned pointer is KVSS_EINVAL.
+ * n == 0 is a no-op; n < 0 or a NULL / misaligned pointer is KVSS_EINVAL; n > 2^31 is
+ * KVSS_EUNSUPPORTED.
  */
 KVSS_API int kvss_philox4x32_10(const uint32_t* counters, int64_t n, uint64_t seed, uint32_t* out,
                                 void* stream);

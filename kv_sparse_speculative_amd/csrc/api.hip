@@ -11,6 +11,7 @@
 
 #include "kvss.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace {
 
@@ -38,45 +39,11 @@ int hip_status(hipError_t e, const char* what) {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-long ceil_div(long a, long b) { return (a + b - 1) / b; }
+using namespace kvss_plan;     // Plan, plan_splits, verify_plan, ceil_div, workgroup targets
 
-// Workgroups a launch should offer: 256 compute units, a few resident workgroups each.
-constexpr long kTargetWorkgroups = 1024;
-// Draft launches: one round of resident workgroups (two per CU).
-constexpr long kDraftTargetWorkgroups = 2 * 256;
-// The SnapKV row-statistics pass keeps two (eight row tiles) or three (fewer) workgroups per
-// CU resident: 3072 workgroups are whole rounds either way (six or four).
-constexpr long kSnapTargetWorkgroups = 3 * 256 * 4;
-constexpr int kMfmaUnit = 128;     // keys one bf16 attention workgroup consumes per round
-constexpr int kSimpleUnit = 32;    // keys one fp32 attention workgroup consumes per round
 constexpr int kMaxGamma = 31;      // speculation length limit of spec_accept
 constexpr int kMaxGridYZ = 65535;  // batch and KV heads index the y / z grid dimensions
 constexpr int kDraftStream = 2;    // Philox stream of the draft-token race
-
-struct Plan {
-    int nsplit;
-    int split_len;
-};
-
-// Split a virtual key range of up to max_total keys per (sequence, KV head) so that the
-// launch offers about `target` workgroups, each doing at least eight rounds (a shorter split
-// would not pay for the extra merge launch and partial traffic); a range shorter than
-// `unsplit_below` keys is not split at all.
-Plan plan_splits(long pairs, long max_total, int unit, long max_len = 1L << 30,
-                 long target = kTargetWorkgroups, long unsplit_below = 0) {
-    Plan p{1, unit};
-    if (max_total <= 0 || pairs <= 0) return p;
-    const long want = ceil_div(target, pairs);
-    const long useful = max_total < unsplit_below ? 1 : ceil_div(max_total, 8L * unit);
-    long ns = want < useful ? want : useful;
-    if (ns < 1) ns = 1;
-    if (ceil_div(max_total, ns) > max_len) ns = ceil_div(max_total, max_len);
-    long len = ceil_div(ceil_div(max_total, ns), unit) * unit;
-    if (len > max_len) len = max_len / unit * unit;
-    p.split_len = (int)len;
-    p.nsplit = (int)ceil_div(max_total, len);
-    return p;
-}
 
 int check_kv(const kvss_kv* kv) {
     if (!kv) return fail(KVSS_EINVAL, "kv descriptor is NULL");
@@ -122,18 +89,6 @@ kvss::AttnArgs attn_common(const kvss_kv* kv) {
 }
 
 float scale_log2(float scale) { return (float)((double)scale * 1.4426950408889634); }
-
-// bf16 verify: contexts under 16k keys are not split. Measured on the Llama-shaped layer (B
-// 32-128, gamma 3-4): an 8k context runs fastest unsplit (no merge launch; whole-sequence
-// workgroups already saturate HBM), while longer contexts gain from the regular plan.
-constexpr long kVerifyUnsplitBelow = 16384;
-
-Plan verify_plan(const kvss_kv* kv) {
-    return kv->dtype == KVSS_BF16
-               ? plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kMfmaUnit,
-                             1L << 30, kTargetWorkgroups, kVerifyUnsplitBelow)
-               : plan_splits((long)kv->batch * kv->num_kv_heads, kv->max_kv_len, kSimpleUnit);
-}
 
 size_t partial_bytes(long rows, const Plan& p, int D) {
     return p.nsplit > 1 ? align_up((size_t)rows * p.nsplit * (D + 2) * sizeof(float)) : 0;
@@ -596,8 +551,8 @@ int kvss_philox4x32_10(const uint32_t* counters, int64_t n, uint64_t seed, uint3
     if (!counters || !out) return fail(KVSS_EINVAL, "counters and out must be non-NULL");
     if (!aligned16(counters) || !aligned16(out))
         return fail(KVSS_EINVAL, "counters and out must be 16-byte aligned");
-    if (n > (int64_t)0xffffffff * 256)
-        return fail(KVSS_EUNSUPPORTED, "n = %lld exceeds the launch limit", (long long)n);
+    if (n > ((int64_t)1 << 31))      // one thread per counter: the grid stays below 2^32 threads
+        return fail(KVSS_EUNSUPPORTED, "n = %lld exceeds 2^31 counters", (long long)n);
     return hip_status(kvss::launch_philox(counters, n, seed, out, static_cast<hipStream_t>(stream)),
                       "philox launch");
 }

@@ -208,3 +208,4 @@ def test_philox_validation():
     assert L.kvss_philox4x32_10(FAKE, 4, 0, None, None) == kvss.KVSS_EINVAL
     assert L.kvss_philox4x32_10(FAKE + 4, 4, 0, FAKE, None) == kvss.KVSS_EINVAL    # misaligned
     assert L.kvss_philox4x32_10(None, 0, 0, None, None) == kvss.KVSS_OK
+    assert L.kvss_philox4x32_10(FAKE, (1 << 31) + 1, 0, FAKE, None) == kvss.KVSS_EUNSUPPORTED
