@@ -111,3 +111,22 @@ def test_snapkv_short_prompts(name):
     o_sel, o_cnt = osnap.select_from_scores(g_c.astype(np.float64), P, w, pool, budget)
     np.testing.assert_array_equal(g_sel, o_sel)
     np.testing.assert_array_equal(g_cnt, o_cnt)
+
+
+@pytest.mark.parametrize("batch", [200, 257])
+def test_verify_ragged_batches_longest_first(batch):
+    """Ragged batches are taken longest first up to 256 sequences (four 64-sequence chunks of
+    the ranking, ties included) and in grid order beyond; every sequence must still land in its
+    own output rows."""
+    ns = _inputs("llama8b_ctx8k", batch, 300)
+    wl = ns.workload
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(1, 300 + ns.T + 1, size=batch).astype(np.int32)
+    lens[::7] = lens[0]                                    # ties
+    t_lens = torch.from_numpy(lens).cuda()
+    kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, t_lens, int(lens.max()))
+    out, lse = kvss.verify_attn_full(kv, ns.q_verify)
+    torch.cuda.synchronize()
+    ref, ref_lse = oatt.verify_attention(host(ns.q_verify), host(ns.k_cache), host(ns.v_cache),
+                                         ns.block_table_np, lens, 1 / math.sqrt(wl.head_dim))
+    _check(out, lse, ref, ref_lse, f"verify ragged B={batch}")
