@@ -7,7 +7,8 @@ Speculative sampling (Leviathan et al., the rule MagicDec Section 3.1 uses) must
     with alpha_i = sum_x min(p_i(x), q_i(x)) (Eq. (1)'s acceptance rate per position);
   * after a rejection at k the emitted token distributed as norm(max(0, p_k - q_k)), and after
     full acceptance the bonus token distributed as p_gamma.
-Each law is checked by a chi-square test at p > 1e-4; impossible tokens must never appear."""
+Each law is checked by a chi-square test at p > 1e-4; impossible tokens must never appear.
+The draft-token sampler is checked the same way against softmax(logits / t)."""
 
 import numpy as np
 import pytest
@@ -78,3 +79,18 @@ def test_speculative_sampling_law_on_the_gpu():
         r = np.maximum(p[k] - q[k], 0.0)
         _chi2(emitted[k], r / r.sum(), f"token after a rejection at {k} ~ norm(max(0, p - q))")
     _chi2(emitted[GAMMA], p[GAMMA], "bonus token after full acceptance ~ p_gamma")
+
+
+@pytest.mark.parametrize("temp", [1.0, 0.6])
+def test_draft_sampler_law_on_the_gpu(temp):
+    """draft_sample at temperature t draws from softmax(logits / t): 2^20 draws, chi-square."""
+    rng = np.random.default_rng(78)
+    z = rng.normal(0.0, 1.5, size=V).astype(np.float32)
+    p = _softmax(z.astype(np.float64) / temp)
+    logits = torch.from_numpy(np.broadcast_to(z, (B, V)).copy()).cuda()
+    counts = np.zeros(V, dtype=np.int64)
+    for c in range(CALLS):
+        tok, _ = kvss.draft_sample(logits, temp, seed=99, offset=c, step=1)
+        torch.cuda.synchronize()
+        counts += np.bincount(tok.cpu().numpy(), minlength=V)
+    _chi2(counts, p, f"draft token at t={temp} ~ softmax(z / t)")
