@@ -104,13 +104,20 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def _need(t, name, dtype=None, device=True):
+def _need(t, name, dtype=None, device=True, shape=None):
+    """Check a tensor the library reads or writes through a raw pointer: contiguous, of the
+    given dtype, on the device and, when `shape` is given, of exactly that shape (the kernels
+    index it by the call's sizes, so a smaller buffer would be read or written out of bounds)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if device and not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 class PagedKV:
@@ -121,7 +128,9 @@ class PagedKV:
         for t, n in ((k, "k"), (v, "v")):
             _need(t, n)
         _need(block_table, "block_table", torch.int32)
-        _need(kv_lens, "kv_lens", torch.int32)
+        if k.dim() != 4 or block_table.dim() != 2:
+            raise ValueError("k, v must be [num_blocks, Hkv, block_size, D]; block_table [B, max_blocks]")
+        _need(kv_lens, "kv_lens", torch.int32, shape=(block_table.shape[0],))
         if k.dtype not in _DTYPE_CODE or v.dtype != k.dtype or v.shape != k.shape:
             raise ValueError("k and v must share shape and a bf16 / f32 dtype")
         self.k, self.v, self.block_table, self.kv_lens = k, v, block_table, kv_lens
@@ -142,10 +151,12 @@ class PagedKV:
 
 
 def _workspace(nbytes, workspace, device):
-    if nbytes == 0:
-        return workspace, 0 if workspace is None else workspace.numel()
+    """The caller's workspace (size checked by the library) or a new one of nbytes."""
     if workspace is None:
+        if nbytes == 0:
+            return None, 0
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _need(workspace, "workspace")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -153,12 +164,17 @@ def verify_attn_full(kv, q, scale=None, out=None, lse=None, want_lse=True, works
                      stream=None):
     """q [B, Hq, T, D] -> (out [B, Hq, T, D] f32, lse [B, Hq, T] f32 or None)."""
     _need(q, "q", kv.dtype)
+    if q.dim() != 4 or q.shape[0] != kv.batch or q.shape[3] != kv.head_dim:
+        raise ValueError("q must be [batch, num_q_heads, T, head_dim] of the cache")
     B, Hq, T, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
         out = torch.empty((B, Hq, T, D), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, shape=(B, Hq, T, D))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq, T))
     d = kv.desc()
     nbytes = lib().kvss_verify_workspace_bytes(ctypes.byref(d), Hq, T)
     workspace, wsb = _workspace(nbytes, workspace, q.device)
@@ -171,17 +187,22 @@ def draft_attn_sparse(kv, q, sel_idx, sel_count, tail_lo, max_tail, scale=None, 
                       lse=None, want_lse=True, workspace=None, stream=None):
     """q [B, Hq, D]; sel_idx int32 [B, Hkv, k_max]; sel_count, tail_lo int32 [B]."""
     _need(q, "q", kv.dtype)
+    if q.dim() != 3 or q.shape[0] != kv.batch or q.shape[2] != kv.head_dim:
+        raise ValueError("q must be [batch, num_q_heads, head_dim] of the cache")
     B, Hq, D = q.shape
     k_max = 0 if sel_idx is None else sel_idx.shape[-1]
     if sel_idx is not None:
-        _need(sel_idx, "sel_idx", torch.int32)
-        _need(sel_count, "sel_count", torch.int32)
-    _need(tail_lo, "tail_lo", torch.int32)
+        _need(sel_idx, "sel_idx", torch.int32, shape=(B, kv.num_kv_heads, k_max))
+        _need(sel_count, "sel_count", torch.int32, shape=(B,))
+    _need(tail_lo, "tail_lo", torch.int32, shape=(B,))
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, shape=(B, Hq, D))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq))
     d = kv.desc()
     nbytes = lib().kvss_draft_workspace_bytes(ctypes.byref(d), Hq, k_max, int(max_tail))
     workspace, wsb = _workspace(nbytes, workspace, q.device)
@@ -204,6 +225,9 @@ def kvss_streaming_set(kv_lens, num_kv_heads, sink, window, sel_idx=None, sel_co
         sel_count = torch.empty(B, dtype=torch.int32, device=dev)
     if tail_lo is None:
         tail_lo = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, shape=(B, num_kv_heads, sink))
+    _need(sel_count, "sel_count", torch.int32, shape=(B,))
+    _need(tail_lo, "tail_lo", torch.int32, shape=(B,))
     _check(lib().kvss_streaming_set(kv_lens.data_ptr(), B, num_kv_heads, sink, window,
                                     sel_idx.data_ptr(), sel_count.data_ptr(), tail_lo.data_ptr(),
                                     _stream(stream)))
@@ -214,6 +238,8 @@ def snapkv_select(kv, q_obs, w, pool_kernel, budget, scale=None, scores_out=None
                   want_scores=False, sel_idx=None, sel_count=None, workspace=None, stream=None):
     """kv.kv_lens = prompt lengths; q_obs [B, Hq, w, D] -> (sel_idx, sel_count, scores|None)."""
     _need(q_obs, "q_obs", kv.dtype)
+    if q_obs.dim() != 4 or q_obs.shape[0] != kv.batch or q_obs.shape[3] != kv.head_dim:
+        raise ValueError("q_obs must be [batch, num_q_heads, w, head_dim] of the cache")
     B, Hq, w_, D = q_obs.shape
     if w_ != w:
         raise ValueError("q_obs window does not match w")
@@ -226,6 +252,11 @@ def snapkv_select(kv, q_obs, w, pool_kernel, budget, scale=None, scores_out=None
     if scores_out is None and want_scores:
         scores_out = torch.zeros((B, kv.num_kv_heads, max(kv.max_kv_len - w, 0)),
                                  dtype=torch.float32, device=dev)
+    _need(sel_idx, "sel_idx", torch.int32, shape=(B, kv.num_kv_heads, budget - w))
+    _need(sel_count, "sel_count", torch.int32, shape=(B,))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.float32,
+              shape=(B, kv.num_kv_heads, max(kv.max_kv_len - w, 0)))
     d = kv.desc()
     nbytes = lib().kvss_snapkv_workspace_bytes(ctypes.byref(d), Hq, w, budget)
     workspace, wsb = _workspace(nbytes, workspace, dev)
@@ -241,11 +272,15 @@ def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, 
     """target [B, gamma+1, V], draft [B, gamma, V] f32; tokens int32 [B, gamma]
     -> (out_tokens [B, gamma+1], num_accepted [B], row_stats [B, 2gamma+1, 4] or None)."""
     _need(target_logits, "target_logits", torch.float32)
-    if draft_logits is not None:
-        _need(draft_logits, "draft_logits", torch.float32)
-    _need(draft_tokens, "draft_tokens", torch.int32)
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [batch, gamma + 1, vocab]")
     B, T, V = target_logits.shape
     gamma = T - 1
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, shape=(B, gamma, V))
+    elif float(temperature) != 0.0 and gamma > 0:
+        raise ValueError("draft_logits are required when temperature > 0 and gamma > 0")
+    _need(draft_tokens, "draft_tokens", torch.int32, shape=(B, gamma))
     dev = target_logits.device
     if out_tokens is None:
         out_tokens = torch.empty((B, T), dtype=torch.int32, device=dev)
@@ -254,6 +289,10 @@ def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, 
         n_acc = torch.empty(B, dtype=torch.int32, device=dev)
     if row_stats is None and want_stats:
         row_stats = torch.zeros((B, 2 * gamma + 1, 4), dtype=torch.float32, device=dev)
+    _need(out_tokens, "out_tokens", torch.int32, shape=(B, T))
+    _need(n_acc, "num_accepted", torch.int32, shape=(B,))
+    if row_stats is not None:
+        _need(row_stats, "row_stats", torch.float32, shape=(B, 2 * gamma + 1, 4))
     nbytes = lib().kvss_accept_workspace_bytes(B, gamma, V)
     workspace, wsb = _workspace(nbytes, workspace, dev)
     _check(lib().spec_accept(target_logits.data_ptr(), _ptr(draft_logits), draft_tokens.data_ptr(),
@@ -279,7 +318,7 @@ def kvss_philox4x32_10(counters, seed, out=None, stream=None):
         raise ValueError("counters must be [n, 4]")
     if out is None:
         out = torch.empty_like(counters)
-    _need(out, "out", torch.int32)
+    _need(out, "out", torch.int32, shape=tuple(counters.shape))
     _check(lib().kvss_philox4x32_10(counters.data_ptr(), counters.shape[0], int(seed) & (2**64 - 1),
                                     out.data_ptr(), _stream(stream)))
     return out
@@ -289,7 +328,7 @@ def kvss_kv_append(kv, k_new, v_new, start, stream=None):
     """Write k_new / v_new [B, Hkv, T, D] at logical positions start[b] + t of the paged cache."""
     _need(k_new, "k_new", kv.dtype)
     _need(v_new, "v_new", kv.dtype)
-    _need(start, "start", torch.int32)
+    _need(start, "start", torch.int32, shape=(kv.batch,))
     B, H, T, D = k_new.shape
     if v_new.shape != k_new.shape or B != kv.batch or H != kv.num_kv_heads or D != kv.head_dim:
         raise ValueError("k_new / v_new must be [batch, num_kv_heads, T, head_dim] of the cache")
@@ -303,12 +342,12 @@ def kvss_draft_cache_build(src, sel_idx, sel_count, tail_lo, max_tail, dst, dst_
     returns dst_lens int32 [B]."""
     k_max = 0 if sel_idx is None else sel_idx.shape[-1]
     if sel_idx is not None:
-        _need(sel_idx, "sel_idx", torch.int32)
-        _need(sel_count, "sel_count", torch.int32)
-    _need(tail_lo, "tail_lo", torch.int32)
+        _need(sel_idx, "sel_idx", torch.int32, shape=(src.batch, src.num_kv_heads, k_max))
+        _need(sel_count, "sel_count", torch.int32, shape=(src.batch,))
+    _need(tail_lo, "tail_lo", torch.int32, shape=(src.batch,))
     if dst_lens is None:
         dst_lens = torch.empty(src.batch, dtype=torch.int32, device=tail_lo.device)
-    _need(dst_lens, "dst_lens", torch.int32)
+    _need(dst_lens, "dst_lens", torch.int32, shape=(src.batch,))
     _check(lib().kvss_draft_cache_build(ctypes.byref(src.desc()), _ptr(sel_idx), _ptr(sel_count),
                                         k_max, tail_lo.data_ptr(), int(max_tail),
                                         ctypes.byref(dst.desc()), dst_lens.data_ptr(),
@@ -321,15 +360,21 @@ def draft_attn_topk(kv, q, k, scale=None, out=None, lse=None, want_lse=True, sel
     """Dynamic Top-K draft: q [B, Hq, D] -> (out [B, Hq, D], lse [B, Hq] or None); the kept
     positions go to sel_idx [B, Hkv, k] / sel_count [B] when given."""
     _need(q, "q", kv.dtype)
+    if q.dim() != 3 or q.shape[0] != kv.batch or q.shape[2] != kv.head_dim:
+        raise ValueError("q must be [batch, num_q_heads, head_dim] of the cache")
     B, Hq, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    for t, n in ((sel_idx, "sel_idx"), (sel_count, "sel_count")):
-        if t is not None:
-            _need(t, n, torch.int32)
+    _need(out, "out", torch.float32, shape=(B, Hq, D))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq))
+    if sel_idx is not None:
+        _need(sel_idx, "sel_idx", torch.int32, shape=(B, kv.num_kv_heads, int(k)))
+    if sel_count is not None:
+        _need(sel_count, "sel_count", torch.int32, shape=(B,))
     d = kv.desc()
     nbytes = lib().kvss_topk_workspace_bytes(ctypes.byref(d), Hq, int(k))
     workspace, wsb = _workspace(nbytes, workspace, q.device)
@@ -343,12 +388,17 @@ def draft_sample(logits, temperature, seed=0, offset=0, step=0, tokens=None, row
                  want_stats=False, workspace=None, stream=None):
     """Draft token per sequence from logits [B, V] f32 -> (tokens int32 [B], row_stats or None)."""
     _need(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [batch, vocab]")
     B, V = logits.shape
     dev = logits.device
     if tokens is None:
         tokens = torch.empty(B, dtype=torch.int32, device=dev)
     if row_stats is None and want_stats:
         row_stats = torch.zeros((B, 4), dtype=torch.float32, device=dev)
+    _need(tokens, "tokens", torch.int32, shape=(B,))
+    if row_stats is not None:
+        _need(row_stats, "row_stats", torch.float32, shape=(B, 4))
     nbytes = lib().kvss_sample_workspace_bytes(B, V)
     workspace, wsb = _workspace(nbytes, workspace, dev)
     _check(lib().draft_sample(logits.data_ptr(), B, V, float(temperature), int(seed) & (2**64 - 1),

@@ -130,3 +130,39 @@ def test_verify_ragged_batches_longest_first(batch):
     ref, ref_lse = oatt.verify_attention(host(ns.q_verify), host(ns.k_cache), host(ns.v_cache),
                                          ns.block_table_np, lens, 1 / math.sqrt(wl.head_dim))
     _check(out, lse, ref, ref_lse, f"verify ragged B={batch}")
+
+
+def test_binding_rejects_mismatched_buffers():
+    """The binding checks every buffer the kernels index by the call's sizes before launching:
+    a wrong shape, dtype or layout raises instead of being read or written out of bounds."""
+    ns = _inputs("llama8b_ctx8k", 2, 64)
+    wl = ns.workload
+    B, Hq, Hkv, T, D = 2, wl.num_q_heads, wl.num_kv_heads, ns.T, wl.head_dim
+    kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.kv_lens_verify, 64 + T)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bad = [
+        lambda: kvss.verify_attn_full(kv, ns.q_verify, out=torch.empty((B, Hq, T - 1, D), **f32)),
+        lambda: kvss.verify_attn_full(kv, ns.q_verify, lse=torch.empty((B, Hq), **f32)),
+        lambda: kvss.verify_attn_full(kv, ns.q_verify[:1].contiguous()),
+        lambda: kvss.verify_attn_full(kv, ns.q_verify.transpose(1, 2)),
+        lambda: kvss.draft_attn_sparse(kv, ns.q_draft, torch.zeros((B, Hkv + 1, 4), **i32),
+                                       torch.zeros(B, **i32), torch.zeros(B, **i32), 8),
+        lambda: kvss.draft_attn_sparse(kv, ns.q_draft, None, None, torch.zeros(B + 1, **i32), 8),
+        lambda: kvss.kvss_streaming_set(ns.kv_lens_draft, Hkv, 4, 60,
+                                        sel_idx=torch.zeros((B, Hkv, 3), **i32)),
+        lambda: kvss.snapkv_select(kv, torch.zeros((B, Hq, 8, D), dtype=torch.bfloat16, device="cuda"),
+                                   8, 3, 16, scores_out=torch.zeros((B, Hkv, 10), **f32)),
+        lambda: kvss.spec_accept(torch.zeros((B, 4, 50), **f32), torch.zeros((B, 3, 50), **f32),
+                                 torch.zeros((B, 3), **i32), 1.0,
+                                 out_tokens=torch.zeros((B, 3), **i32)),
+        lambda: kvss.spec_accept(torch.zeros((B, 4, 50), **f32), None, torch.zeros((B, 3), **i32),
+                                 1.0),
+        lambda: kvss.draft_sample(torch.zeros((B, 50), **f32), 1.0,
+                                  tokens=torch.zeros(B, dtype=torch.int64, device="cuda")),
+        lambda: kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, torch.zeros(B + 1, **i32), 64),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
