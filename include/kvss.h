@@ -19,6 +19,8 @@
  * and the cache maintenance around them (Section 3.1; Appendix A.1, Fig. 8):
  *   kvss_kv_append          append the newly scored tokens' K/V rows to a paged cache
  *   kvss_draft_cache_build  materialise the compressed draft cache once at prefill
+ * plus kvss_philox4x32_10 (the generator behind every sampled draw, to replay one) and
+ * kvss_stream_read (a plain read, the bandwidth reference the kernels are measured against).
  *
  * Conventions (all calls)
  *   - Every pointer argument that names a tensor is a DEVICE pointer owned by the caller; the
