@@ -425,6 +425,7 @@ def cpu_baseline(wl, ns, sink, window, budget_s=12.0):
     nbytes = 0
     steps = 0
     t0 = time.perf_counter()
+    c0 = time.process_time()
     with threadpool_limits(limits=cores):
         while True:
             c = osnap.snapkv_scores(q_obs, kh, table, p0, w, 1 / math.sqrt(wl.head_dim), pairs=[(0, 0)])
@@ -449,10 +450,13 @@ def cpu_baseline(wl, ns, sink, window, budget_s=12.0):
             if time.perf_counter() - t0 >= budget_s:
                 break
     dt = time.perf_counter() - t0
+    busy = (time.process_time() - c0) / dt          # CPU seconds per wall second: cores in use
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "busy_cores": round(busy, 2),
             "sample": (f"{steps} step(s) of sequence 0 / KV head 0 (SnapKV select, StreamingLLM "
                        f"draft, verify, SnapKV draft) plus sequence 0's acceptance, "
-                       f"{dt:.1f} s wall")}
+                       f"{dt:.1f} s wall; numpy with a BLAS pool of {cores} threads, "
+                       f"{busy:.2f} cores busy on average")}
 
 
 def main():
