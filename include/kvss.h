@@ -243,6 +243,7 @@ KVSS_API int draft_attn_topk(const kvss_kv* kv, const void* q, int num_q_heads, 
  *   step       draft step index within the round, in [0, 65535]
  *   tokens     int32 [batch] (device), written
  *   row_stats  nullable float [batch, 4]: max of z / t, sum of exp(z / t - max), 0, argmax
+ *              (at temperature 0 only the argmax is meaningful: the first two are 0)
  * Workspace: kvss_sample_workspace_bytes(batch, vocab). vocab < 2^24; batch <= 65535
  * (KVSS_EUNSUPPORTED above).
  */

@@ -44,6 +44,7 @@ def test_draft_sample_matches_oracle(name, batch, vocab, temp):
                                   [oacc.argmax_lowest(r) for r in z])
     if temp == 0:
         np.testing.assert_array_equal(g, ref)
+        assert (host(st)[:, :3] == 0).all()        # greedy: only the argmax is written
         return
     np.testing.assert_allclose(host(st)[:, 0], z.max(axis=1) / temp, rtol=1e-6)
     # sum of exp(z / t - max): float32 terms summed over the row, relative error << 1e-4
@@ -91,6 +92,7 @@ def test_draft_sample_scalar_path(vocab, shift, temp):
     np.testing.assert_array_equal(host(st)[:, 3].astype(np.int64), [oacc.argmax_lowest(r) for r in z])
     if temp == 0:
         np.testing.assert_array_equal(g, ref)
+        assert (host(st)[:, :3] == 0).all()        # greedy: only the argmax is written
         return
     ref_s = np.exp(z / temp - (z / temp).max(axis=1, keepdims=True)).sum(axis=1)
     np.testing.assert_allclose(host(st)[:, 1], ref_s, rtol=1e-4)
