@@ -202,7 +202,8 @@ KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads
  *                    0..gamma, then draft rows 0..gamma-1) the max of z / temperature, the sum
  *                    of exp(z / temperature - max), z / temperature at the row's draft token
  *                    (0 for the last target row), and the argmax as a float. With
- *                    temperature == 0 only the argmax of target rows is filled (others 0).
+ *                    temperature == 0 only the argmax of target rows is filled; every other
+ *                    entry, the draft rows included, is written as 0.
  */
 KVSS_API size_t kvss_accept_workspace_bytes(int batch, int gamma, int vocab);
 KVSS_API int spec_accept(const float* target_logits, const float* draft_logits,

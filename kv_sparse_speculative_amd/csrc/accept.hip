@@ -193,6 +193,12 @@ __global__ __launch_bounds__(64) void accept_decide_kernel(AcceptArgs a, const P
             o[3] = (float)bi;
         }
     }
+    // greedy reads no draft rows: their statistics rows are written as zeros
+    if (greedy && a.stats != nullptr)
+        for (int r = rows + lane; r < 2 * gamma + 1; r += 64) {
+            float* o = a.stats + ((size_t)b * (2 * gamma + 1) + r) * 4;
+            o[0] = 0.f; o[1] = 0.f; o[2] = 0.f; o[3] = 0.f;
+        }
     __syncthreads();
     if (lane != 0) return;
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);

@@ -2,7 +2,8 @@
 queries whose causal range is empty or a single key (sequences shorter than T, an empty
 cache), drafts over empty, single-key and partly invalid selections (entries past the tail or
 the sequence, a negative or over-long tail start), and SnapKV on prompts no longer than the
-window, with fewer candidates than the budget, exactly the budget, and one more."""
+window, with fewer candidates than the budget, exactly the budget, and one more; and the
+acceptance statistics buffer written in full, whatever the temperature."""
 
 import math
 
@@ -166,3 +167,24 @@ def test_binding_rejects_mismatched_buffers():
         with pytest.raises(ValueError):
             call()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("gamma", [0, 1, 3])
+def test_accept_statistics_rows_written_in_full(gamma):
+    """Every entry of the caller's statistics buffer is written: at temperature 0 the target
+    rows carry only the argmax and the draft rows are zeros; sampling fills every row."""
+    ns = generate(WORKLOADS["llama8b_ctx8k"], device="cuda", batch=5, parts=("accept",),
+                  vocab=3000)
+    target = ns.target_logits[:, : gamma + 1].contiguous()
+    draft = ns.draft_logits[:, :gamma].contiguous()
+    tokens = ns.draft_tokens[:, :gamma].contiguous()
+    z = host(target).astype(np.float64)
+    for temp in (0.0, 1.0):
+        st = torch.full((5, 2 * gamma + 1, 4), float("nan"), dtype=torch.float32, device="cuda")
+        kvss.spec_accept(target, draft, tokens, temp, 3, 1, row_stats=st)
+        torch.cuda.synchronize()
+        s = host(st)
+        assert not np.isnan(s).any(), temp
+        np.testing.assert_array_equal(s[:, : gamma + 1, 3].astype(np.int64), z.argmax(axis=2))
+        if temp == 0:
+            assert (s[:, : gamma + 1, :3] == 0).all() and (s[:, gamma + 1:] == 0).all()
