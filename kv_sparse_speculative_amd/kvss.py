@@ -150,12 +150,17 @@ class PagedKV:
         return self._desc
 
 
-def _workspace(nbytes, workspace, device):
-    """The caller's workspace (size checked by the library) or a new one of nbytes."""
+def _workspace(nbytes, workspace, device, stream=None):
+    """The caller's workspace (size checked by the library) or a new one of nbytes. A new one
+    comes from torch's allocator on the current stream and is dropped when the call returns,
+    while the kernels may still run: on another stream it is recorded there, so the allocator
+    does not hand its memory out before that stream has passed this call."""
     if workspace is None:
         if nbytes == 0:
             return None, 0
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if stream is not None and stream != torch.cuda.current_stream(device):
+            workspace.record_stream(stream)
     _need(workspace, "workspace")
     return workspace, workspace.numel() * workspace.element_size()
 
@@ -177,7 +182,7 @@ def verify_attn_full(kv, q, scale=None, out=None, lse=None, want_lse=True, works
         _need(lse, "lse", torch.float32, shape=(B, Hq, T))
     d = kv.desc()
     nbytes = lib().kvss_verify_workspace_bytes(ctypes.byref(d), Hq, T)
-    workspace, wsb = _workspace(nbytes, workspace, q.device)
+    workspace, wsb = _workspace(nbytes, workspace, q.device, stream)
     _check(lib().verify_attn_full(ctypes.byref(d), q.data_ptr(), Hq, T, scale, out.data_ptr(),
                                   _ptr(lse), _ptr(workspace), wsb, _stream(stream)))
     return out, lse
@@ -205,7 +210,7 @@ def draft_attn_sparse(kv, q, sel_idx, sel_count, tail_lo, max_tail, scale=None, 
         _need(lse, "lse", torch.float32, shape=(B, Hq))
     d = kv.desc()
     nbytes = lib().kvss_draft_workspace_bytes(ctypes.byref(d), Hq, k_max, int(max_tail))
-    workspace, wsb = _workspace(nbytes, workspace, q.device)
+    workspace, wsb = _workspace(nbytes, workspace, q.device, stream)
     _check(lib().draft_attn_sparse(ctypes.byref(d), q.data_ptr(), Hq, _ptr(sel_idx),
                                    _ptr(sel_count), k_max, tail_lo.data_ptr(), int(max_tail),
                                    scale, out.data_ptr(), _ptr(lse), _ptr(workspace), wsb,
@@ -259,7 +264,7 @@ def snapkv_select(kv, q_obs, w, pool_kernel, budget, scale=None, scores_out=None
               shape=(B, kv.num_kv_heads, max(kv.max_kv_len - w, 0)))
     d = kv.desc()
     nbytes = lib().kvss_snapkv_workspace_bytes(ctypes.byref(d), Hq, w, budget)
-    workspace, wsb = _workspace(nbytes, workspace, dev)
+    workspace, wsb = _workspace(nbytes, workspace, dev, stream)
     _check(lib().snapkv_select(ctypes.byref(d), q_obs.data_ptr(), Hq, w, pool_kernel, budget,
                                scale, sel_idx.data_ptr(), sel_count.data_ptr(), _ptr(scores_out),
                                _ptr(workspace), wsb, _stream(stream)))
@@ -294,7 +299,7 @@ def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, 
     if row_stats is not None:
         _need(row_stats, "row_stats", torch.float32, shape=(B, 2 * gamma + 1, 4))
     nbytes = lib().kvss_accept_workspace_bytes(B, gamma, V)
-    workspace, wsb = _workspace(nbytes, workspace, dev)
+    workspace, wsb = _workspace(nbytes, workspace, dev, stream)
     _check(lib().spec_accept(target_logits.data_ptr(), _ptr(draft_logits), draft_tokens.data_ptr(),
                              B, gamma, V, float(temperature), int(seed) & (2**64 - 1),
                              int(offset) & (2**64 - 1), out_tokens.data_ptr(), n_acc.data_ptr(),
@@ -377,7 +382,7 @@ def draft_attn_topk(kv, q, k, scale=None, out=None, lse=None, want_lse=True, sel
         _need(sel_count, "sel_count", torch.int32, shape=(B,))
     d = kv.desc()
     nbytes = lib().kvss_topk_workspace_bytes(ctypes.byref(d), Hq, int(k))
-    workspace, wsb = _workspace(nbytes, workspace, q.device)
+    workspace, wsb = _workspace(nbytes, workspace, q.device, stream)
     _check(lib().draft_attn_topk(ctypes.byref(d), q.data_ptr(), Hq, int(k), scale, out.data_ptr(),
                                  _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), wsb,
                                  _stream(stream)))
@@ -400,7 +405,7 @@ def draft_sample(logits, temperature, seed=0, offset=0, step=0, tokens=None, row
     if row_stats is not None:
         _need(row_stats, "row_stats", torch.float32, shape=(B, 4))
     nbytes = lib().kvss_sample_workspace_bytes(B, V)
-    workspace, wsb = _workspace(nbytes, workspace, dev)
+    workspace, wsb = _workspace(nbytes, workspace, dev, stream)
     _check(lib().draft_sample(logits.data_ptr(), B, V, float(temperature), int(seed) & (2**64 - 1),
                               int(offset) & (2**64 - 1), int(step), tokens.data_ptr(),
                               _ptr(row_stats), _ptr(workspace), wsb, _stream(stream)))

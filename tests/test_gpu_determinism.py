@@ -8,6 +8,8 @@ and the same cache copied into an identity layout must agree bit for bit (SnapKV
 kept sets, gathered drafts, the dynamic Top-K draft and the compact draft cache built from it).
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -102,4 +104,46 @@ def test_samplers_repeat(temp):
         torch.cuda.synchronize()
         runs.append((out, n_acc, stats, tok, st))
     for x, y in zip(*runs):
+        assert torch.equal(x, y)
+
+
+def test_calls_on_a_side_stream_match_the_current_stream():
+    """`stream=` runs a call on another stream. The workspace the binding allocates is recorded
+    on that stream, so memory claimed and overwritten on the current stream straight after the
+    call cannot be the workspace still in use (the split partials, the SnapKV scores)."""
+    torch.manual_seed(0)
+    ns = generate(WORKLOADS["llama8b_ctx32k"], device="cuda", parts=("attn",), batch=4,
+                  prompt=(20000, 20000))
+    wl = ns.workload
+    budget, w, pool = wl.snapkv
+    P = ns.prompt_lens_np
+    kv_v = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.kv_lens_verify,
+                        int(P.max()) + ns.T)
+    kv_p = kv_v.with_lens(ns.prompt_lens, int(P.max()))
+
+    lib = kvss.lib()
+    ws_v = lib.kvss_verify_workspace_bytes(ctypes.byref(kv_v.desc()), wl.num_q_heads, ns.T)
+    ws_s = lib.kvss_snapkv_workspace_bytes(ctypes.byref(kv_p.desc()), wl.num_q_heads, w, budget)
+    assert ws_v > 0 and ws_s > 0
+
+    def churn(nbytes, value):
+        # blocks of the size the binding just freed, claimed and overwritten at once
+        return [torch.full((nbytes,), value, dtype=torch.uint8, device="cuda") for _ in range(4)]
+
+    def run(stream):
+        o, l = kvss.verify_attn_full(kv_v, ns.q_verify, stream=stream)
+        held = churn(ws_v, 7)
+        sel, cnt, sc = kvss.snapkv_select(kv_p, ns.q_obs, w, pool, budget, want_scores=True,
+                                          stream=stream)
+        held += churn(ws_s, 3)
+        del held
+        return o, l, sel, cnt, sc
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = run(side)
+    side.synchronize()
+    for x, y in zip(ref, got):
         assert torch.equal(x, y)
