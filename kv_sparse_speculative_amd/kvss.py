@@ -7,6 +7,8 @@ kernels; there is no fallback. Loading fails loudly if libkvss.so has not been b
 """
 
 import ctypes
+import functools
+import inspect
 import math
 import os
 import re
@@ -104,6 +106,24 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _on_call_stream(fn):
+    """Run a wrapper with its `stream` argument (when given) as torch's current stream, so that
+    the outputs and the workspace the wrapper allocates, and the fills of those it zeroes, are
+    ordered on the stream the library's kernels run on; memory the wrapper drops on return
+    then goes back to that stream's pool, which the allocator hands out only to later work on
+    the same stream."""
+    idx = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        stream = kwargs.get("stream", args[idx] if len(args) > idx else None)
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return call
+
+
 def _need(t, name, dtype=None, device=True, shape=None):
     """Check a tensor the library reads or writes through a raw pointer: contiguous, of the
     given dtype, on the device and, when `shape` is given, of exactly that shape (the kernels
@@ -150,21 +170,18 @@ class PagedKV:
         return self._desc
 
 
-def _workspace(nbytes, workspace, device, stream=None):
-    """The caller's workspace (size checked by the library) or a new one of nbytes. A new one
-    comes from torch's allocator on the current stream and is dropped when the call returns,
-    while the kernels may still run: on another stream it is recorded there, so the allocator
-    does not hand its memory out before that stream has passed this call."""
+def _workspace(nbytes, workspace, device):
+    """The caller's workspace (size checked by the library) or a new one of nbytes, allocated
+    on the stream the call runs on (see `_on_call_stream`)."""
     if workspace is None:
         if nbytes == 0:
             return None, 0
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        if stream is not None and stream != torch.cuda.current_stream(device):
-            workspace.record_stream(stream)
     _need(workspace, "workspace")
     return workspace, workspace.numel() * workspace.element_size()
 
 
+@_on_call_stream
 def verify_attn_full(kv, q, scale=None, out=None, lse=None, want_lse=True, workspace=None,
                      stream=None):
     """q [B, Hq, T, D] -> (out [B, Hq, T, D] f32, lse [B, Hq, T] f32 or None)."""
@@ -182,12 +199,13 @@ def verify_attn_full(kv, q, scale=None, out=None, lse=None, want_lse=True, works
         _need(lse, "lse", torch.float32, shape=(B, Hq, T))
     d = kv.desc()
     nbytes = lib().kvss_verify_workspace_bytes(ctypes.byref(d), Hq, T)
-    workspace, wsb = _workspace(nbytes, workspace, q.device, stream)
+    workspace, wsb = _workspace(nbytes, workspace, q.device)
     _check(lib().verify_attn_full(ctypes.byref(d), q.data_ptr(), Hq, T, scale, out.data_ptr(),
                                   _ptr(lse), _ptr(workspace), wsb, _stream(stream)))
     return out, lse
 
 
+@_on_call_stream
 def draft_attn_sparse(kv, q, sel_idx, sel_count, tail_lo, max_tail, scale=None, out=None,
                       lse=None, want_lse=True, workspace=None, stream=None):
     """q [B, Hq, D]; sel_idx int32 [B, Hkv, k_max]; sel_count, tail_lo int32 [B]."""
@@ -210,7 +228,7 @@ def draft_attn_sparse(kv, q, sel_idx, sel_count, tail_lo, max_tail, scale=None, 
         _need(lse, "lse", torch.float32, shape=(B, Hq))
     d = kv.desc()
     nbytes = lib().kvss_draft_workspace_bytes(ctypes.byref(d), Hq, k_max, int(max_tail))
-    workspace, wsb = _workspace(nbytes, workspace, q.device, stream)
+    workspace, wsb = _workspace(nbytes, workspace, q.device)
     _check(lib().draft_attn_sparse(ctypes.byref(d), q.data_ptr(), Hq, _ptr(sel_idx),
                                    _ptr(sel_count), k_max, tail_lo.data_ptr(), int(max_tail),
                                    scale, out.data_ptr(), _ptr(lse), _ptr(workspace), wsb,
@@ -218,6 +236,7 @@ def draft_attn_sparse(kv, q, sel_idx, sel_count, tail_lo, max_tail, scale=None, 
     return out, lse
 
 
+@_on_call_stream
 def kvss_streaming_set(kv_lens, num_kv_heads, sink, window, sel_idx=None, sel_count=None,
                        tail_lo=None, stream=None):
     """StreamingLLM set -> (sel_idx [B, Hkv, sink], sel_count [B], tail_lo [B]) int32."""
@@ -239,6 +258,7 @@ def kvss_streaming_set(kv_lens, num_kv_heads, sink, window, sel_idx=None, sel_co
     return sel_idx, sel_count, tail_lo
 
 
+@_on_call_stream
 def snapkv_select(kv, q_obs, w, pool_kernel, budget, scale=None, scores_out=None,
                   want_scores=False, sel_idx=None, sel_count=None, workspace=None, stream=None):
     """kv.kv_lens = prompt lengths; q_obs [B, Hq, w, D] -> (sel_idx, sel_count, scores|None)."""
@@ -264,13 +284,14 @@ def snapkv_select(kv, q_obs, w, pool_kernel, budget, scale=None, scores_out=None
               shape=(B, kv.num_kv_heads, max(kv.max_kv_len - w, 0)))
     d = kv.desc()
     nbytes = lib().kvss_snapkv_workspace_bytes(ctypes.byref(d), Hq, w, budget)
-    workspace, wsb = _workspace(nbytes, workspace, dev, stream)
+    workspace, wsb = _workspace(nbytes, workspace, dev)
     _check(lib().snapkv_select(ctypes.byref(d), q_obs.data_ptr(), Hq, w, pool_kernel, budget,
                                scale, sel_idx.data_ptr(), sel_count.data_ptr(), _ptr(scores_out),
                                _ptr(workspace), wsb, _stream(stream)))
     return sel_idx, sel_count, scores_out
 
 
+@_on_call_stream
 def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, offset=0,
                 row_stats=None, want_stats=False, out_tokens=None, num_accepted=None,
                 workspace=None, stream=None):
@@ -299,7 +320,7 @@ def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, 
     if row_stats is not None:
         _need(row_stats, "row_stats", torch.float32, shape=(B, 2 * gamma + 1, 4))
     nbytes = lib().kvss_accept_workspace_bytes(B, gamma, V)
-    workspace, wsb = _workspace(nbytes, workspace, dev, stream)
+    workspace, wsb = _workspace(nbytes, workspace, dev)
     _check(lib().spec_accept(target_logits.data_ptr(), _ptr(draft_logits), draft_tokens.data_ptr(),
                              B, gamma, V, float(temperature), int(seed) & (2**64 - 1),
                              int(offset) & (2**64 - 1), out_tokens.data_ptr(), n_acc.data_ptr(),
@@ -307,6 +328,7 @@ def spec_accept(target_logits, draft_logits, draft_tokens, temperature, seed=0, 
     return out_tokens, n_acc, row_stats
 
 
+@_on_call_stream
 def kvss_stream_read(buf, sink, stream=None):
     """Measurement reference: stream-read every byte of the device tensor `buf`."""
     _need(buf, "buf")
@@ -315,6 +337,7 @@ def kvss_stream_read(buf, sink, stream=None):
                                   _stream(stream)))
 
 
+@_on_call_stream
 def kvss_philox4x32_10(counters, seed, out=None, stream=None):
     """The library's Philox4x32-10 on counters int32/uint32-bit words [n, 4] (device, stored as
     torch.int32); returns the output words [n, 4] as torch.int32 bit patterns."""
@@ -329,6 +352,7 @@ def kvss_philox4x32_10(counters, seed, out=None, stream=None):
     return out
 
 
+@_on_call_stream
 def kvss_kv_append(kv, k_new, v_new, start, stream=None):
     """Write k_new / v_new [B, Hkv, T, D] at logical positions start[b] + t of the paged cache."""
     _need(k_new, "k_new", kv.dtype)
@@ -341,6 +365,7 @@ def kvss_kv_append(kv, k_new, v_new, start, stream=None):
                                 start.data_ptr(), _stream(stream)))
 
 
+@_on_call_stream
 def kvss_draft_cache_build(src, sel_idx, sel_count, tail_lo, max_tail, dst, dst_lens=None,
                            stream=None):
     """Compact draft cache: dst receives each (b, g)'s listed rows then the tail of src;
@@ -360,6 +385,7 @@ def kvss_draft_cache_build(src, sel_idx, sel_count, tail_lo, max_tail, dst, dst_
     return dst_lens
 
 
+@_on_call_stream
 def draft_attn_topk(kv, q, k, scale=None, out=None, lse=None, want_lse=True, sel_idx=None,
                     sel_count=None, workspace=None, stream=None):
     """Dynamic Top-K draft: q [B, Hq, D] -> (out [B, Hq, D], lse [B, Hq] or None); the kept
@@ -382,13 +408,14 @@ def draft_attn_topk(kv, q, k, scale=None, out=None, lse=None, want_lse=True, sel
         _need(sel_count, "sel_count", torch.int32, shape=(B,))
     d = kv.desc()
     nbytes = lib().kvss_topk_workspace_bytes(ctypes.byref(d), Hq, int(k))
-    workspace, wsb = _workspace(nbytes, workspace, q.device, stream)
+    workspace, wsb = _workspace(nbytes, workspace, q.device)
     _check(lib().draft_attn_topk(ctypes.byref(d), q.data_ptr(), Hq, int(k), scale, out.data_ptr(),
                                  _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), wsb,
                                  _stream(stream)))
     return out, lse
 
 
+@_on_call_stream
 def draft_sample(logits, temperature, seed=0, offset=0, step=0, tokens=None, row_stats=None,
                  want_stats=False, workspace=None, stream=None):
     """Draft token per sequence from logits [B, V] f32 -> (tokens int32 [B], row_stats or None)."""
@@ -405,7 +432,7 @@ def draft_sample(logits, temperature, seed=0, offset=0, step=0, tokens=None, row
     if row_stats is not None:
         _need(row_stats, "row_stats", torch.float32, shape=(B, 4))
     nbytes = lib().kvss_sample_workspace_bytes(B, V)
-    workspace, wsb = _workspace(nbytes, workspace, dev, stream)
+    workspace, wsb = _workspace(nbytes, workspace, dev)
     _check(lib().draft_sample(logits.data_ptr(), B, V, float(temperature), int(seed) & (2**64 - 1),
                               int(offset) & (2**64 - 1), int(step), tokens.data_ptr(),
                               _ptr(row_stats), _ptr(workspace), wsb, _stream(stream)))

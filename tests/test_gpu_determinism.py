@@ -108,9 +108,10 @@ def test_samplers_repeat(temp):
 
 
 def test_calls_on_a_side_stream_match_the_current_stream():
-    """`stream=` runs a call on another stream. The workspace the binding allocates is recorded
-    on that stream, so memory claimed and overwritten on the current stream straight after the
-    call cannot be the workspace still in use (the split partials, the SnapKV scores)."""
+    """`stream=` runs a call on another stream. The binding allocates the call's outputs and
+    workspace (and zero-fills the SnapKV scores) on that stream, so the fills are ordered before
+    the kernels, and memory claimed and overwritten on the current stream straight after the
+    call cannot be a workspace still in use (the split partials, the SnapKV scores)."""
     torch.manual_seed(0)
     ns = generate(WORKLOADS["llama8b_ctx32k"], device="cuda", parts=("attn",), batch=4,
                   prompt=(20000, 20000))
