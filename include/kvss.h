@@ -24,9 +24,11 @@
  *
  * Conventions (all calls)
  *   - Every pointer argument that names a tensor is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or retains device memory. Scratch space comes from the
- *     caller's `workspace` buffer, whose required size the matching *_workspace_bytes query
- *     returns for the same shape arguments (0 is a valid size; workspace may then be NULL).
+ *     library never allocates, frees or retains device memory (the one exception is the fixed
+ *     per-GPU scratch array of verify_attn_full_noalloc, part of the loaded code object).
+ *     Scratch space comes from the caller's `workspace` buffer, whose required size the
+ *     matching *_workspace_bytes query returns for the same shape arguments (0 is a valid
+ *     size; workspace may then be NULL).
  *     A workspace must not be shared by calls that may run concurrently.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls enqueue
  *     kernels and return without synchronising; outputs are valid once the stream has
@@ -116,6 +118,25 @@ KVSS_API size_t kvss_verify_workspace_bytes(const kvss_kv* kv, int num_q_heads, 
 KVSS_API int verify_attn_full(const kvss_kv* kv, const void* q, int num_q_heads, int T, float scale,
                      float* out, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * verify_attn_full_noalloc -- verify_attn_full for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It
+ * computes exactly what verify_attn_full computes, with the same kernels and split plan, so
+ * the results are bit-identical; the split partials live in a device array the library owns
+ * instead of a caller workspace.
+ *   Arguments as for verify_attn_full, without the workspace.
+ *   Scratch limit: 32 MiB (33554432 bytes). A shape whose kvss_verify_workspace_bytes exceeds
+ *   it returns KVSS_EWORKSPACE and enqueues nothing; every shape with a workspace need of 0
+ *   (an unsplit plan) is accepted.
+ *   The array is one per GPU, holds its 32 MiB until the process ends, and keeps the last
+ *   call's contents (nothing in it needs to start at zero). The first call on a device looks
+ *   its address up (hipGetSymbolAddress), preferably outside graph capture. Calls that may
+ *   overlap on one GPU (other streams, other threads) race on the array: serialise them.
+ *   No hipMalloc, hipFree or allocating library routine is called.
+ */
+KVSS_API int verify_attn_full_noalloc(const kvss_kv* kv, const void* q, int num_q_heads, int T,
+                                      float scale, float* out, float* lse, void* stream);
 
 /*
  * draft_attn_sparse -- one draft query per sequence over a sparse subset of the cache.

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "kvss.h"
@@ -154,6 +155,68 @@ bool temperature_ok(float t) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------------------
+// verify_attn_full_noalloc: the same verify, with its split partials in a library-owned
+// device array instead of a caller workspace, for callers that cannot allocate.
+
+// Largest split-partial area the no-allocation verify accepts: the plan asks for about 1024
+// workgroups, so [B * Hq * T, nsplit, D + 2] floats stay near 2048 * G * T * (D + 2) * 4
+// bytes, ~11 MB at G * T = 20 and head_dim 128.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
+// One copy per GPU the library runs on, held until the process ends. In host code the name
+// stands for a host-side shadow, not a device address: kernels get the per-device address
+// that scratch_on_current_device() looks up.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device).
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KVSS_EUNSUPPORTED, "device ordinal %d is beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(KVSS_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+
+}  // namespace
+
+extern "C" int verify_attn_full_noalloc(const kvss_kv* kv, const void* q, int num_q_heads, int T,
+                                        float scale, float* out, float* lse, void* stream) {
+    int rc = check_kv(kv);
+    if (rc) return rc;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (T <= 0) return fail(KVSS_EINVAL, "T (gamma + 1) must be >= 1 (got %d)", T);
+    const int G = num_q_heads / kv->num_kv_heads;
+    if (G * T > 32) return fail(KVSS_EUNSUPPORTED, "G * T = %d exceeds 32 query rows per KV head", G * T);
+    if (!isfinite(scale)) return fail(KVSS_EINVAL, "scale must be finite");
+    if (kv->batch == 0) return ok();
+    if (!q || !out) return fail(KVSS_EINVAL, "q and out must be non-NULL");
+    const size_t need = kvss_verify_workspace_bytes(kv, num_q_heads, T);
+    if (need > kNoAllocScratchBytes)
+        return fail(KVSS_EWORKSPACE,
+                    "split partials of %zu bytes exceed the %zu-byte no-allocation scratch; "
+                    "use verify_attn_full with a workspace", need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && (rc = scratch_on_current_device(&ws))) return rc;
+    return verify_attn_full(kv, q, num_q_heads, T, scale, out, lse, ws, need, stream);
+}
 
 extern "C" {
 

@@ -51,6 +51,7 @@ _SIGNATURES = {
     "kvss_version": (_I, []),
     "kvss_verify_workspace_bytes": (_Z, [_KV, _I, _I]),
     "verify_attn_full": (_I, [_KV, _P, _I, _I, _F, _P, _P, _P, _Z, _P]),
+    "verify_attn_full_noalloc": (_I, [_KV, _P, _I, _I, _F, _P, _P, _P]),
     "kvss_draft_workspace_bytes": (_Z, [_KV, _I, _I, _I]),
     "draft_attn_sparse": (_I, [_KV, _P, _I, _P, _P, _I, _P, _I, _F, _P, _P, _P, _Z, _P]),
     "kvss_streaming_set": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
@@ -202,6 +203,28 @@ def verify_attn_full(kv, q, scale=None, out=None, lse=None, want_lse=True, works
     workspace, wsb = _workspace(nbytes, workspace, q.device)
     _check(lib().verify_attn_full(ctypes.byref(d), q.data_ptr(), Hq, T, scale, out.data_ptr(),
                                   _ptr(lse), _ptr(workspace), wsb, _stream(stream)))
+    return out, lse
+
+
+@_on_call_stream
+def verify_attn_full_noalloc(kv, q, scale=None, out=None, lse=None, want_lse=True, stream=None):
+    """verify_attn_full with the split partials in the library's own device scratch (no
+    workspace). q [B, Hq, T, D] -> (out, lse or None); out / lse are allocated here only when
+    not given, so a caller that passes both allocates nothing."""
+    _need(q, "q", kv.dtype)
+    if q.dim() != 4 or q.shape[0] != kv.batch or q.shape[3] != kv.head_dim:
+        raise ValueError("q must be [batch, num_q_heads, T, head_dim] of the cache")
+    B, Hq, T, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, Hq, T, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, shape=(B, Hq, T, D))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq, T))
+    _check(lib().verify_attn_full_noalloc(ctypes.byref(kv.desc()), q.data_ptr(), Hq, T, scale,
+                                          out.data_ptr(), _ptr(lse), _stream(stream)))
     return out, lse
 
 

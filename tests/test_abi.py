@@ -209,3 +209,25 @@ def test_philox_validation():
     assert L.kvss_philox4x32_10(FAKE + 4, 4, 0, FAKE, None) == kvss.KVSS_EINVAL    # misaligned
     assert L.kvss_philox4x32_10(None, 0, 0, None, None) == kvss.KVSS_OK
     assert L.kvss_philox4x32_10(FAKE, (1 << 31) + 1, 0, FAKE, None) == kvss.KVSS_EUNSUPPORTED
+
+
+def _verify_noalloc(d, Hq=8, T=5, q=FAKE, out=FAKE, scale=0.1):
+    return kvss.lib().verify_attn_full_noalloc(ctypes.byref(d), q, Hq, T, scale, out, None, None)
+
+
+def test_noalloc_verify_validation_and_scratch_limit():
+    d = _desc()
+    assert _verify_noalloc(d, Hq=7) == kvss.KVSS_EINVAL
+    assert _verify_noalloc(d, T=0) == kvss.KVSS_EINVAL
+    assert _verify_noalloc(d, Hq=16, T=5) == kvss.KVSS_EUNSUPPORTED
+    assert _verify_noalloc(d, out=None) == kvss.KVSS_EINVAL
+    assert _verify_noalloc(_desc(head_dim=96)) == kvss.KVSS_EUNSUPPORTED
+    assert _verify_noalloc(_desc(batch=0, k=None, v=None, block_table=None, kv_lens=None)) == kvss.KVSS_OK
+    # 1023 (sequence, KV head) pairs with 32 query rows each, split in two: 34,045,440 bytes of
+    # partials, beyond the 32 MiB scratch -> rejected before any HIP call
+    big = _desc(batch=1023, num_kv_heads=1, max_blocks=1300, num_blocks=1 << 20, max_kv_len=20000)
+    need = kvss.lib().kvss_verify_workspace_bytes(ctypes.byref(big), 4, 8)
+    assert need > 32 << 20
+    assert _verify_noalloc(big, Hq=4, T=8) == kvss.KVSS_EWORKSPACE
+    msg = kvss.lib().kvss_last_error().decode()
+    assert "scratch" in msg and str(need) in msg
