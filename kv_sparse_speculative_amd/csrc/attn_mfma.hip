@@ -11,7 +11,9 @@
 // each wave takes 32-key chunks of the split round-robin.
 //   Prologue: the workgroup translates the split's keys into physical cache rows once (block
 //     table, and for a draft the selection list) into an LDS table, so no dependent global
-//     read sits in front of a K/V load in the main loop.
+//     read sits in front of a K/V load in the main loop. For a draft the selection-list reads
+//     do not wait for the sequence's lengths: the prologue costs two round trips (lengths,
+//     list and queries together; then the block table).
 //   Main loop, register double-buffered: the K and V rows of the wave's next chunk are in
 //     flight while the current chunk is computed:
 //     S^T (16 keys x 16 rows tiles) = K . Q^T with v_mfma_f32_16x16x32_bf16; K rows come from
@@ -19,12 +21,14 @@
 //       registers as the B operand;
 //     online softmax in the log2 domain (row max across the 4 lane groups with xor shuffles;
 //       each lane owns one query row of the C tile);
-//     O^T (16 dims x 16 rows) += V^T . P^T with P split into bf16 hi + lo parts (two MFMAs) so
-//       that P carries ~16 mantissa bits; V^T is read transposed from a padded LDS tile that
-//       the same wave wrote V rows arrive
-//       with row-contiguous nontemporal loads (each instruction covers whole rows, the pattern
-//       that keeps the HBM read rate highest); K rows, used straight from registers as the
-//       MFMA operand, keep plain loads (routing K through LDS as well measured slower).
+//     O^T (16 dims x 16 rows) += V^T . P^T with P split into bf16 hi + lo parts so that P
+//       carries ~16 mantissa bits: two MFMAs, or, when the tile has room for twice the query
+//       rows (R <= 8: a draft, or a one-token decode), one MFMA whose rows R .. 2R - 1 repeat
+//       the queries and carry the lo parts; V^T is read transposed from a padded LDS tile that
+//       the same wave wrote: V rows arrive with row-contiguous nontemporal loads (each
+//       instruction covers whole rows, the pattern that keeps the HBM read rate highest); K
+//       rows, used straight from registers as the MFMA operand, keep plain loads (routing K
+//       through LDS as well measured slower).
 // Waves merge (max, sum, O) through LDS; with one split the workgroup writes the final
 // normalised output, otherwise (m, l, o) partials that the merge kernel combines.
 // Over the full cache, sequences are taken longest first (see the kernel's prologue).
@@ -40,6 +44,9 @@ constexpr unsigned kInvalidRow = 0xffffffffu;
 // Largest batch whose workgroups order themselves longest-first (each ranks every sequence:
 // O(B^2 / 64) work per workgroup).
 constexpr int kLongestFirstMaxBatch = 256;
+// Table entries each thread of a draft workgroup fills per pass (1024 keys per pass: one pass
+// covers a draft set of up to 1024 keys per split).
+constexpr int kSelUnroll = 4;
 
 template <int D, int NRT>
 struct MfmaCfg {
@@ -53,8 +60,8 @@ struct MfmaCfg {
     static constexpr int SMEM = (VLDS + TAB) > MERGE ? (VLDS + TAB) : MERGE;
 };
 
-// Entries of the physical-row table one thread fills per pass of the prologue; their global
-// reads are all issued before any is waited on.
+// Entries of the physical-row table one thread fills per pass of the dense prologue; their
+// global reads are all issued before any is waited on.
 constexpr int kTabUnroll = 4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
@@ -110,9 +117,11 @@ __device__ __forceinline__ int longest_first(const AttnArgs& a, int z, int lane)
 }
 
 // With one row tile the kernel fits two workgroups per CU (<= 256 registers per lane), so a
-// draft launch of B * Hkv workgroups is resident in a single round.
-template <int D, bool GATHER, int NRT>
+// draft launch of B * Hkv workgroups is resident in a single round. FOLD (one row tile, R <= 8
+// query rows) puts the lo parts of P in tile rows R .. 2R - 1 instead of a second MFMA.
+template <int D, bool GATHER, int NRT, bool FOLD>
 __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
+    static_assert(!FOLD || NRT == 1, "folded hi/lo rows need a single row tile");
     using C = MfmaCfg<D, NRT>;
     constexpr int NBUF = 2;            // chunks in flight per wave
     constexpr int KS = C::KS, DT = C::DT, STRIDE = C::STRIDE, ROWS = C::ROWS;
@@ -132,45 +141,81 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     if constexpr (!GATHER) {
         if (a.B > 1 && a.B <= kLongestFirstMaxBatch) b = longest_first(a, blockIdx.z, lane);
     }
-
-    const int L = max(min(a.kv_lens[b], a.max_kv_len), 0);
-    int n_list = 0, lo = 0;
-    if constexpr (GATHER) {
-        n_list = min(max(a.sel_count[b], 0), a.k_max);
-        lo = min(max(a.tail_lo[b], 0), L);
-    }
-    const int total = n_list + (L - lo);
     const int v_begin = split * a.split_len;
-    const int v_end = (split == a.nsplit - 1) ? total : min(v_begin + a.split_len, total);
+    const int32_t* sel = GATHER ? a.sel_idx + ((size_t)b * a.Hkv + g) * a.k_max : nullptr;
+    const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
+    unsigned* rowtab = reinterpret_cast<unsigned*>(smem + C::VLDS);
 
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k);
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v);
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-    const int bs = a.bs, sh = (bs & (bs - 1)) == 0 ? __builtin_ctz(bs) : -1;
+    // Draft prologue: the first pass of selection entries, the queries and the sequence's
+    // lengths are all requested before any of them is waited for, so together they cost one
+    // round trip (the block-table reads that depend on them are the second). Entry v < k_max is
+    // read whatever the count turns out to be; whether it is listed is decided once the count
+    // is known.
+    int sv0[GATHER ? kSelUnroll : 1];
+    if constexpr (GATHER) {
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+            const int v = v_begin + u * kWaves * 64 + tid;
+            sv0[u] = v < a.k_max ? sel[v] : 0;
+        }
+    }
 
     // Q^T as the B operand: lane supplies column (row) rt*16 + m16, dims ks*32 + q4*8 .. +7.
+    // Folded: columns R .. 2R - 1 repeat query rows 0 .. R - 1. (Issued with the prologue's
+    // other loads: the queries do not depend on the lengths.)
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     bf16x8 qop[NRT][KS];
-    int limit[NRT];
+    int qrow[NRT];                     // query row of this lane's column, or -1
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-        const int r = rt * 16 + m16;
-        limit[rt] = -1;
+        int r = rt * 16 + m16;
+        if (FOLD && r >= a.R && r < 2 * a.R) r -= a.R;
+        qrow[rt] = r < a.R ? r : -1;
         if (r < a.R) {
             const int h = g * a.G + r / a.T, t = r % a.T;
             const uint16_t* src = qp + (((size_t)b * a.Hq + h) * a.T + t) * D + q4 * 8;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 qop[rt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + ks * 32));
-            limit[rt] = GATHER ? 0x7fffffff : L - a.T + t;
         } else {
             // zero queries: finite scores, never written out, and no causal bound
-            limit[rt] = 0x7fffffff;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
         }
     }
+
+    // The sequence's lengths. For a draft, lanes 0, 1, 2 fetch them with one vector load issued
+    // after the loads above, so one wait covers all of them (plain uniform loads would be scalar
+    // loads, which the compiler issues only after waiting for the vector loads: a second round
+    // trip).
+    int L, n_list = 0, lo = 0;
+    if constexpr (GATHER) {
+        const int32_t* lp = lane == 0 ? a.kv_lens : (lane == 1 ? a.sel_count : a.tail_lo);
+        const int x = lane < 3 ? lp[b] : 0;
+        L = __builtin_amdgcn_readlane(x, 0);
+        n_list = __builtin_amdgcn_readlane(x, 1);
+        lo = __builtin_amdgcn_readlane(x, 2);
+        L = max(min(L, a.max_kv_len), 0);
+        n_list = min(max(n_list, 0), a.k_max);
+        lo = min(max(lo, 0), L);
+    } else {
+        L = max(min(a.kv_lens[b], a.max_kv_len), 0);
+    }
+    const int total = n_list + (L - lo);
+    const int v_end = (split == a.nsplit - 1) ? total : min(v_begin + a.split_len, total);
+
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k);
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v);
+    const int bs = a.bs, sh = (bs & (bs - 1)) == 0 ? __builtin_ctz(bs) : -1;
+
+    int limit[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+        limit[rt] = (GATHER || qrow[rt] < 0) ? 0x7fffffff : L - a.T + qrow[rt] % a.T;
     // Every key below this position is visible to every query row (the first causal row).
     const int lim_all = GATHER ? 0x7fffffff : L - a.T;
+    // Folded: lanes of rows R .. 2R - 1 feed the lo parts of P to the PV product.
+    const bool lo_lane = FOLD && m16 >= a.R && m16 < 2 * a.R;
 
     f32x4 o[DT][NRT];
 #pragma unroll
@@ -182,58 +227,73 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     for (int rt = 0; rt < NRT; ++rt) { mrow[rt] = kNegInf; lrow[rt] = 0.f; }
 
     uint16_t* vl = reinterpret_cast<uint16_t*>(smem) + wid * 32 * STRIDE;
-    unsigned* rowtab = reinterpret_cast<unsigned*>(smem + C::VLDS);
-    const int32_t* sel = GATHER ? a.sel_idx + ((size_t)b * a.Hkv + g) * a.k_max : nullptr;
-    const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
+
+    // Draft table fill, one pass: rowtab[i] for i = base + u * 256 + tid (u < kSelUnroll) =
+    // physical row of key v = seg + i of [seg, seg_end), from the selection entries sv and the
+    // block table. All of a thread's block-table reads are issued before any is used.
+    auto fill_gather = [&](int seg, int seg_end, int base, const int (&sv)[kSelUnroll]) {
+        const int n = seg_end - seg;
+        int pos[kSelUnroll];
+        bool ok[kSelUnroll];
+        int blk[kSelUnroll];
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+            const int v = seg + base + u * kWaves * 64 + tid;
+            const bool listed = v < n_list;
+            pos[u] = listed ? sv[u] : lo + (v - n_list);
+            ok[u] = v < seg_end && (!listed || (sv[u] >= 0 && sv[u] < lo));
+            blk[u] = btab[ok[u] ? div_bs(pos[u], bs, sh) : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+            const int i = base + u * kWaves * 64 + tid;
+            if (i >= n) continue;
+            unsigned row = kInvalidRow;
+            if (ok[u]) {
+                if ((unsigned)blk[u] < (unsigned)a.num_blocks)
+                    row = ((unsigned)blk[u] * a.Hkv + g) * bs + (pos[u] - div_bs(pos[u], bs, sh) * bs);
+                else
+                    s_bad = 1;
+            }
+            rowtab[i] = row;
+        }
+    };
+    // Later passes of a draft table (sets of more than 1024 keys per split): their selection
+    // entries are read in the pass.
+    auto fill_rest = [&](int seg, int seg_end, int from) {
+        for (int base = from; base < seg_end - seg; base += kSelUnroll * kWaves * 64) {
+            int sv[kSelUnroll];
+#pragma unroll
+            for (int u = 0; u < kSelUnroll; ++u) {
+                const int v = seg + base + u * kWaves * 64 + tid;
+                sv[u] = v < a.k_max ? sel[v] : 0;
+            }
+            fill_gather(seg, seg_end, base, sv);
+        }
+    };
+    if constexpr (GATHER) {
+        // First segment, first pass: its selection entries are already in registers (they die
+        // here, before the main loop).
+        __syncthreads();                               // s_bad is initialised
+        const int seg_end0 = min(v_begin + kMfmaTableEntries, v_end);
+        if (v_begin < v_end) {
+            fill_gather(v_begin, seg_end0, 0, sv0);
+            fill_rest(v_begin, seg_end0, kSelUnroll * kWaves * 64);
+        }
+    }
 
     // Segment = the keys whose rows one LDS table holds (the planner keeps a split to one).
     const int seg_keys = GATHER ? kMfmaTableEntries : kMfmaTableEntries * bs;
     for (int seg = v_begin; seg < v_end; seg += seg_keys) {
         const int seg_end = min(seg + seg_keys, v_end);
         const int blk0 = seg / bs;
-        __syncthreads();                          // previous segment's table is no longer read
         if constexpr (GATHER) {
-            const int n = seg_end - seg;
-            for (int base = 0; base < n; base += kTabUnroll * kWaves * 64) {
-                int pos[kTabUnroll];
-                bool ok[kTabUnroll];
-                // Reads are unconditional (indices clamped into range) so that all of a
-                // thread's selection reads, then all of its block-table reads, are in flight
-                // together.
-                int sv[kTabUnroll];
-#pragma unroll
-                for (int u = 0; u < kTabUnroll; ++u) {       // selection-list reads
-                    const int v = seg + base + u * kWaves * 64 + tid;
-                    sv[u] = n_list > 0 ? sel[min(max(v, 0), n_list - 1)] : 0;
-                }
-#pragma unroll
-                for (int u = 0; u < kTabUnroll; ++u) {
-                    const int v = seg + base + u * kWaves * 64 + tid;
-                    const bool listed = v < n_list;
-                    pos[u] = listed ? sv[u] : lo + (v - n_list);
-                    ok[u] = v < seg_end && (!listed || (sv[u] >= 0 && sv[u] < lo));
-                }
-                int blk[kTabUnroll];
-#pragma unroll
-                for (int u = 0; u < kTabUnroll; ++u) {       // block-table reads
-                    const int bi = ok[u] ? pos[u] / bs : 0;
-                    blk[u] = btab[bi];
-                }
-#pragma unroll
-                for (int u = 0; u < kTabUnroll; ++u) {
-                    const int i = base + u * kWaves * 64 + tid;
-                    if (i >= n) continue;
-                    unsigned row = kInvalidRow;
-                    if (ok[u]) {
-                        if ((unsigned)blk[u] < (unsigned)a.num_blocks)
-                            row = ((unsigned)blk[u] * a.Hkv + g) * bs + pos[u] % bs;
-                        else
-                            s_bad = 1;
-                    }
-                    rowtab[i] = row;
-                }
+            if (seg != v_begin) {           // a split longer than one table: refill it
+                __syncthreads();            // the previous segment's table is no longer read
+                fill_rest(seg, seg_end, 0);
             }
         } else {
+            __syncthreads();                // the previous segment's table is no longer read
             const int nblk = (seg_end - 1) / bs - blk0 + 1;
             for (int base = 0; base < nblk; base += kTabUnroll * kWaves * 64) {
                 int blk[kTabUnroll];
@@ -389,8 +449,13 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
                 for (int j = 0; j < 8; ++j) {
                     const float p = __builtin_amdgcn_exp2f(sv[j] - muse);
                     const __bf16 hi = (__bf16)p;
-                    phi[rt][j] = hi;
-                    plo[rt][j] = (__bf16)(p - (float)hi);
+                    const __bf16 lo_part = (__bf16)(p - (float)hi);
+                    if constexpr (FOLD) {
+                        phi[rt][j] = lo_lane ? lo_part : hi;
+                    } else {
+                        phi[rt][j] = hi;
+                        plo[rt][j] = lo_part;
+                    }
                     psum += p;
                 }
                 lrow[rt] += psum;
@@ -419,7 +484,8 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt) {
                     o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi[rt], o[dt][rt], 0, 0, 0);
-                    o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo[rt], o[dt][rt], 0, 0, 0);
+                    if constexpr (!FOLD)
+                        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo[rt], o[dt][rt], 0, 0, 0);
                 }
             }
             wave_lds_order();
@@ -455,13 +521,17 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     __syncthreads();                 // every wave is done with its V tile (smem is reused)
     float* so = reinterpret_cast<float*>(smem);               // [wave][ROWS][D]
     float* sml = so + kWaves * ROWS * D;                       // [wave][ROWS][2]
+    // Rows that reach the output: R (and, folded, the lo rows R .. 2R - 1).
+    const int live = FOLD ? 2 * a.R : ROWS;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
+            if (rt * 16 + m16 < live) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                so[(wid * ROWS + rt * 16 + m16) * D + dt * 16 + q4 * 4 + i] = o[dt][rt][i];
+                for (int i = 0; i < 4; ++i)
+                    so[(wid * ROWS + rt * 16 + m16) * D + dt * 16 + q4 * 4 + i] = o[dt][rt][i];
+            }
     if (q4 == 0) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
@@ -483,8 +553,10 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float e = __builtin_amdgcn_exp2f(sml[(w * ROWS + r) * 2] - M);
+                float ow = so[(w * ROWS + r) * D + d];
+                if constexpr (FOLD) ow += so[(w * ROWS + r + a.R) * D + d];
                 lsum += e * sml[(w * ROWS + r) * 2 + 1];
-                osum += e * so[(w * ROWS + r) * D + d];
+                osum += e * ow;
             }
         }
         const int h = g * a.G + r / a.T, t = r % a.T;
@@ -508,23 +580,25 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     }
 }
 
-template <int D, int NRT>
+template <int D, int NRT, bool FOLD>
 void launch_d(const AttnArgs& a, bool gather, dim3 grid, dim3 block, hipStream_t s) {
-    if (gather) attn_mfma_kernel<D, true, NRT><<<grid, block, 0, s>>>(a);
-    else attn_mfma_kernel<D, false, NRT><<<grid, block, 0, s>>>(a);
+    if (gather) attn_mfma_kernel<D, true, NRT, FOLD><<<grid, block, 0, s>>>(a);
+    else attn_mfma_kernel<D, false, NRT, FOLD><<<grid, block, 0, s>>>(a);
 }
 
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool gather, hipStream_t s) {
     dim3 grid(a.nsplit, a.Hkv, a.B), block(kWaves * 64);
-    const bool one = a.R <= 16;
+    const bool one = a.R <= 16, fold = a.R <= 8;
     if (a.D == 128) {
-        if (one) launch_d<128, 1>(a, gather, grid, block, s);
-        else launch_d<128, 2>(a, gather, grid, block, s);
+        if (fold) launch_d<128, 1, true>(a, gather, grid, block, s);
+        else if (one) launch_d<128, 1, false>(a, gather, grid, block, s);
+        else launch_d<128, 2, false>(a, gather, grid, block, s);
     } else {
-        if (one) launch_d<64, 1>(a, gather, grid, block, s);
-        else launch_d<64, 2>(a, gather, grid, block, s);
+        if (fold) launch_d<64, 1, true>(a, gather, grid, block, s);
+        else if (one) launch_d<64, 1, false>(a, gather, grid, block, s);
+        else launch_d<64, 2, false>(a, gather, grid, block, s);
     }
     return hipGetLastError();
 }
