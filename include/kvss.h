@@ -206,7 +206,8 @@ KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads
  *   [batch, gamma], each in [0, vocab).
  *   temperature == 0: greedy. Draft token i is accepted while it equals the target argmax at
  *     position i (ties: lowest id); the first mismatch emits the target argmax there; if all
- *     match, the argmax at position gamma is appended.
+ *     match, the argmax at position gamma is appended. The argmax is taken over a row's non-NaN
+ *     logits; a row with none has argmax -1, which then is the emitted token.
  *   temperature > 0: rejection sampling with p = softmax(target / temperature), q = softmax(
  *     draft / temperature). Position i accepts when u_i < p_i(x_i) / q_i(x_i); the first
  *     rejection emits a draw from max(0, p_i - q_i) (from p_i if that is all zero); if all are
@@ -216,13 +217,15 @@ KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads
  *     offset low 32 bits); stream 0 word 0 gives u_i, stream 1 word x % 4 of block x / 4
  *     gives u'_x; a 32-bit word x maps to (x >> 9) * 2^-23 + 2^-24. Callers advance `offset`
  *     between calls that share a seed.
+ *   Rows holding NaN or no finite logit give unspecified sampling draws (never an error).
  *   Limits: 0 <= gamma <= 31 and batch <= 65535 (KVSS_EUNSUPPORTED above), 1 <= vocab < 2^24.
  *   out_tokens       int32 [batch, gamma + 1]: emitted tokens, then -1.
  *   out_num_accepted int32 [batch]: accepted draft tokens, 0 .. gamma.
  *   row_stats        float32 [batch, 2 * gamma + 1, 4] or NULL: per logit row (target rows
  *                    0..gamma, then draft rows 0..gamma-1) the max of z / temperature, the sum
  *                    of exp(z / temperature - max), z / temperature at the row's draft token
- *                    (0 for the last target row), and the argmax as a float. With
+ *                    (0 for the last target row), and the argmax as a float (-1 for a row
+ *                    with no non-NaN logit). With
  *                    temperature == 0 only the argmax of target rows is filled; every other
  *                    entry, the draft rows included, is written as 0.
  */
@@ -257,7 +260,8 @@ KVSS_API int draft_attn_topk(const kvss_kv* kv, const void* q, int num_q_heads, 
 /*
  * draft_sample -- the draft token of one draft step (MagicDec Section 3.1: the draft proposes
  * the gamma tokens the target verifies; Section 5.1 drafts greedily). From the draft's logits
- * [batch, vocab] (fp32): temperature 0 takes the argmax (ties to the lowest id); temperature
+ * [batch, vocab] (fp32): temperature 0 takes the argmax over the non-NaN logits (ties to the
+ * lowest id; -1 for a row with none); temperature
  * t > 0 draws from softmax(logits / t) by the exponential race spec_accept uses, on a Philox
  * stream of its own (stream 2, position `step`, same key and offset conventions), so the draft
  * token and the later acceptance draws are independent. The normaliser of softmax is common to

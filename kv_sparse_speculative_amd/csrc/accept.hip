@@ -7,13 +7,20 @@
 //            partial (a reference r, the sum of 2^(z log2(e) / temp - r), max z, its lowest
 //            index); the reference moves only when a term would pass 2^64, so the common block
 //            of 4 tokens costs four fma + exp2 and no data-dependent branch;
-//   decide   one wave per sequence: merges the partials into row statistics, walks the gamma
-//            accept tests (greedy argmax match, or u_i < p_i(x_i) / q_i(x_i) with Philox
-//            uniforms) and writes the accepted prefix, the count and the emitting position;
+//   decide   one wave per sequence, a lane per logit row: merges each row's partials into its
+//            statistics, runs the gamma accept tests in parallel lanes (greedy argmax match, or
+//            u_i < p_i(x_i) / q_i(x_i) with Philox uniforms), takes the first failing lane, and
+//            writes the accepted prefix, the count, and the emitting position with the merged
+//            statistics of its rows (so the race reads one record, not the partials);
 //   race     (sampling only) grid (slice, sequence): exponential race argmin_x -log(u'_x) / w(x)
 //            over one slice of the emitting row, w = max(0, p - q) after a rejection (p if that
-//            is all zero) or p after full acceptance; re-reads only that row pair;
-//   finalize (sampling only) one wave per sequence: the winning token of the slices.
+//            is all zero) or p after full acceptance; re-reads only that row pair, several
+//            16-byte loads in flight per thread;
+//   finalize (sampling only) one wave per sequence: the winning token of the slices, merged
+//            across lanes.
+// Argmax: the lowest index of the maximum over the row's non-NaN entries; a row with no such
+// entry has argmax -1. The streaming passes track only entries above -inf; a row without one is
+// rescanned by the decide kernel (its argmax is then its first non-NaN entry).
 
 #include "common.h"
 #include "launch.h"
@@ -39,8 +46,12 @@ struct RaceKey {
 
 struct Decision {      // per sequence
     int pos;           // emitting position (= number accepted)
+    float ct, rst;     // emitting target row: (max of z / t) * log2(e), 1 / (sum of exp)
+    float cd, rsd;     // emitting draft row after a rejection (0 after full acceptance)
     int pad[3];
 };
+
+constexpr int kNoArgmax = 0x7fffffff;   // no non-NaN entry seen
 
 // (reference, sum) pairs in the log2 domain
 __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
@@ -66,18 +77,45 @@ __device__ __forceinline__ const float* row_ptr(const AcceptArgs& a, int b, int 
 
 // Statistics of one logit row from its slice partials: m = max of z / t (exactly (max z) / t:
 // rounding is monotone), s = sum of exp(z / t - m), and the argmax.
+// The partials are read eight at a time (all eight loads in flight), then merged in slice
+// order.
 __device__ __forceinline__ void row_stats(const Part* p, int nslice, float it, bool greedy,
                                           float& m, float& s, float& best, int& bi) {
+    constexpr int kBatch = 8;
     float m2 = kNegInf, s2 = 0.f;
     best = kNegInf;
-    bi = 0x7fffffff;
-    for (int k = 0; k < nslice; ++k) {
-        if (!greedy) ms_merge(m2, s2, p[k].m2, p[k].s);
-        am_merge(best, bi, p[k].zmax, p[k].imax);
+    bi = kNoArgmax;
+    for (int k0 = 0; k0 < nslice; k0 += kBatch) {
+        Part q[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            q[u] = k0 + u < nslice ? p[k0 + u] : Part{kNegInf, 0.f, kNegInf, kNoArgmax};
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (!greedy) ms_merge(m2, s2, q[u].m2, q[u].s);
+            am_merge(best, bi, q[u].zmax, q[u].imax);
+        }
     }
     m = best * it;
     s = 0.f;
     if (!greedy && best != kNegInf) s = s2 * __builtin_amdgcn_exp2f(m2 - best * (it * kLog2e));
+}
+
+// Lowest index of a non-NaN entry of row z[0, V), or -1; the whole wave scans (used only for a
+// row in which no entry exceeds -inf, whose argmax is then its first -inf entry).
+__device__ int first_non_nan(const float* z, int V, int lane) {
+    int found = 0x7fffffff;
+    for (int x0 = 0; x0 < V; x0 += 8 * 64) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = x0 + u * 64 + lane < V ? z[x0 + u * 64 + lane] : __builtin_nanf("");
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (v[u] == v[u]) found = min(found, x0 + u * 64 + lane);
+        for (int o = 32; o > 0; o >>= 1) found = min(found, __shfl_xor(found, o));
+        if (found != 0x7fffffff) return found;
+    }
+    return -1;
 }
 
 template <bool GREEDY>
@@ -94,7 +132,7 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a
     const int u0 = slice * per, u1 = min(units, u0 + per);
     const float c = a.inv_temp * kLog2e;
     float m = kNegInf, s = 0.f, best = kNegInf;
-    int bi = 0x7fffffff;
+    int bi = kNoArgmax;
     // Block of n <= 4 tokens x0 .. x0 + n - 1. The sum keeps a lazy reference m: a block's terms
     // 2^(z c - m) are added as they are unless their sum leaves [0, 2^64] (a score more than 64
     // above m, or the first block with m = -inf); only then does m move to the block's max.
@@ -166,31 +204,43 @@ __global__ __launch_bounds__(kStatThreads) void accept_stats_kernel(AcceptArgs a
     }
 }
 
-// One wave per sequence: row statistics, accept walk, accepted prefix.
+// One wave per sequence: a lane per logit row merges that row's statistics; lane i < gamma
+// runs accept test i; the first failing lane is the emitting position.
 __global__ __launch_bounds__(64) void accept_decide_kernel(AcceptArgs a, const Part* parts,
                                                            int nslice, int rows,
                                                            Decision* dec) {
-    __shared__ float st[64][4];
+    __shared__ float sm[64], ss[64], szx[64];
+    __shared__ int sarg[64];
     const int b = blockIdx.x, lane = threadIdx.x;
     const int gamma = a.gamma, V = a.V;
     const bool greedy = a.inv_temp == 0.f;
-    for (int r = lane; r < rows; r += 64) {
-        float m, s, best;
-        int bi;
-        row_stats(parts + ((size_t)b * rows + r) * nslice, nslice, a.inv_temp, greedy, m, s, best, bi);
-        float zx = 0.f;
-        if (!greedy && r != gamma) {
-            const int i = (r < gamma) ? r : r - gamma - 1;
-            const int x = a.tokens[(size_t)b * gamma + i];
-            zx = (x >= 0 && x < V) ? row_ptr(a, b, r)[x] * a.inv_temp : kNegInf;
-        }
-        if (r < 64) { st[r][0] = m; st[r][1] = s; st[r][2] = zx; st[r][3] = (float)bi; }
+    // this lane's draft token (lanes i < gamma: position i; draft rows gamma+1+i: position i)
+    const int ti = lane < gamma ? lane : lane - gamma - 1;
+    const bool has_tok = (lane < gamma) || (!greedy && lane > gamma && lane < rows);
+    const int x = has_tok ? a.tokens[(size_t)b * gamma + ti] : -1;
+    float m = 0.f, s = 0.f, zx = 0.f;
+    int bi = kNoArgmax;
+    if (lane < rows) {
+        float best;
+        row_stats(parts + ((size_t)b * rows + lane) * nslice, nslice, a.inv_temp, greedy, m, s, best, bi);
+        if (!greedy && lane != gamma) zx = (x >= 0 && x < V) ? row_ptr(a, b, lane)[x] * a.inv_temp : kNegInf;
+    }
+    // A row in which no entry exceeds -inf: its argmax is its first non-NaN entry (-1 if none).
+    for (unsigned long long need = __ballot(lane < rows && bi == kNoArgmax); need != 0ull;
+         need &= need - 1) {
+        const int r = __ffsll((long long)need) - 1;
+        const int arg = first_non_nan(row_ptr(a, b, r), V, lane);
+        if (lane == r) bi = arg;
+    }
+    if (lane < rows) {
+        const int arg = bi;
+        sm[lane] = m; ss[lane] = s; szx[lane] = zx; sarg[lane] = arg;
         if (a.stats != nullptr) {
-            float* o = a.stats + ((size_t)b * (2 * gamma + 1) + r) * 4;
+            float* o = a.stats + ((size_t)b * (2 * gamma + 1) + lane) * 4;
             o[0] = greedy ? 0.f : m;
             o[1] = greedy ? 0.f : s;
             o[2] = zx;
-            o[3] = (float)bi;
+            o[3] = (float)arg;
         }
     }
     // greedy reads no draft rows: their statistics rows are written as zeros
@@ -200,58 +250,58 @@ __global__ __launch_bounds__(64) void accept_decide_kernel(AcceptArgs a, const P
             o[0] = 0.f; o[1] = 0.f; o[2] = 0.f; o[3] = 0.f;
         }
     __syncthreads();
-    if (lane != 0) return;
-    const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
-    int32_t* out = a.out_tokens + (size_t)b * (gamma + 1);
-    int n = 0;
-    for (; n < gamma; ++n) {
-        const int x = a.tokens[(size_t)b * gamma + n];
-        bool ok;
+    bool ok = true;
+    if (lane < gamma) {
         if (greedy) {
-            ok = (int)st[n][3] == x;
+            ok = x >= 0 && sarg[lane] == x;
         } else {
             // p(x) / q(x) as one exp2 of a difference of logs: at a low temperature p(x) and
             // q(x) alone can underflow float while their ratio is ordinary.
-            const float* t = st[n];
-            const float* d = st[gamma + 1 + n];
-            const float lp = (t[2] - t[0]) * kLog2e - __log2f(t[1]);
-            const float lq = (d[2] - d[0]) * kLog2e - __log2f(d[1]);
-            uint32_t c0 = 0, c1 = (uint32_t)n, c2 = (uint32_t)b, c3 = (uint32_t)a.offset;
-            philox4x32_10(c0, c1, c2, c3, k0, k1);
+            const int d = gamma + 1 + lane;
+            const float lp = (szx[lane] - sm[lane]) * kLog2e - __log2f(ss[lane]);
+            const float lq = (szx[d] - sm[d]) * kLog2e - __log2f(ss[d]);
+            uint32_t c0 = 0, c1 = (uint32_t)lane, c2 = (uint32_t)b, c3 = (uint32_t)a.offset;
+            philox4x32_10(c0, c1, c2, c3, (uint32_t)a.seed, (uint32_t)(a.seed >> 32));
             ok = (x >= 0 && x < V) && philox_uniform(c0) < __builtin_amdgcn_exp2f(lp - lq);
         }
-        if (!ok) break;
-        out[n] = x;
     }
-    for (int j = n + 1; j <= gamma; ++j) out[j] = -1;
-    a.out_num[b] = n;
-    if (greedy) out[n] = (int)st[n][3];
-    dec[b].pos = n;
+    const unsigned long long fail = __ballot(!ok);
+    const int n = fail ? __ffsll((long long)fail) - 1 : gamma;
+    int32_t* out = a.out_tokens + (size_t)b * (gamma + 1);
+    if (lane < n) out[lane] = x;
+    else if (lane == n) out[lane] = greedy ? sarg[n] : -1;     // sampling: the race fills it
+    else if (lane <= gamma) out[lane] = -1;
+    if (lane == 0) {
+        a.out_num[b] = n;
+        Decision r{};
+        r.pos = n;
+        if (!greedy) {
+            r.ct = sm[n] * kLog2e;
+            r.rst = 1.f / ss[n];
+            if (n < gamma) {
+                r.cd = sm[gamma + 1 + n] * kLog2e;
+                r.rsd = 1.f / ss[gamma + 1 + n];
+            }
+        }
+        dec[b] = r;
+    }
 }
 
 // Exponential race over one slice of the emitting row of one sequence.
-__global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a, const Part* parts,
-                                                                   int nslice, int rows,
-                                                                   const Decision* dec,
+__global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a, const Decision* dec,
                                                                    RaceKey* race, int nrace) {
     __shared__ RaceKey sr[kRaceThreads / 64], sq[kRaceThreads / 64];
     const int slice = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int gamma = a.gamma, V = a.V;
-    const int pos = dec[b].pos;
+    // the emitting position and its rows' statistics, merged once by the decide kernel
+    const Decision d = dec[b];
+    const int pos = d.pos;
     const bool residual = pos < gamma;
-    // merged statistics of the two rows (identical arithmetic to the decide kernel)
-    float mt, st, md = kNegInf, sd = 0.f, zm;
-    int zi;
-    row_stats(parts + ((size_t)b * rows + pos) * nslice, nslice, a.inv_temp, false, mt, st, zm, zi);
-    if (residual)
-        row_stats(parts + ((size_t)b * rows + gamma + 1 + pos) * nslice, nslice, a.inv_temp, false,
-                  md, sd, zm, zi);
     const float* zt = a.target + ((size_t)b * (gamma + 1) + pos) * V;
     const float* zd = residual ? a.draft + ((size_t)b * gamma + pos) * V : nullptr;
     // p(x) = 2^(z(x) * it * log2e - m * log2e) / s, evaluated as one FMA and one v_exp.
     const float c1 = a.inv_temp * kLog2e;
-    const float ct = mt * kLog2e, cd = md * kLog2e;
-    const float rst = 1.f / st, rsd = residual ? 1.f / sd : 0.f;
+    const float ct = d.ct, cd = d.cd, rst = d.rst, rsd = d.rsd;
     const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
     const uint32_t off = (uint32_t)a.offset;
     const int nblk = (V + 3) / 4;
@@ -261,9 +311,47 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
     // rows are read as one 16-byte load per block of 4 tokens when they are 16-byte aligned
     const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(zt) & 15) == 0 &&
                      (!residual || (reinterpret_cast<uintptr_t>(zd) & 15) == 0);
-    for (int j = j0 + tid; j < j1; j += kRaceThreads) {
+    // One block of 4 tokens: its Philox words, then each token's race keys.
+    auto block = [&](int j, const float (&vt)[4], const float (&vd)[4]) {
         uint32_t w0 = (uint32_t)j, w1 = ((uint32_t)kRaceStream << 16) | (uint32_t)pos,
                  w2 = (uint32_t)b, w3 = off;
+        philox4x32_10(w0, w1, w2, w3, k0, k1);
+        const uint32_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = 4 * j + e;
+            if (x >= V) break;
+            const float E = -__builtin_amdgcn_logf(philox_uniform(w[e])) * kLn2;
+            const float pt = __builtin_amdgcn_exp2f(fmaf(vt[e], c1, -ct)) * rst;
+            if (residual) {        // (the race over p itself is needed only if no rr > 0)
+                const float pd = __builtin_amdgcn_exp2f(fmaf(vd[e], c1, -cd)) * rsd;
+                const float rr = pt - pd;
+                if (rr > 0.f) race_merge(br, {E * __builtin_amdgcn_rcpf(rr), x});
+            } else if (pt > 0.f) {
+                race_merge(bp, {E * __builtin_amdgcn_rcpf(pt), x});
+            }
+        }
+    };
+    constexpr int kBatch = 4;                   // 16-byte loads in flight per thread and row
+    int j = j0 + tid;
+    if (vec) {
+        const float4* t4p = reinterpret_cast<const float4*>(zt);
+        const float4* d4p = reinterpret_cast<const float4*>(zd);
+        for (; j + (kBatch - 1) * kRaceThreads < j1; j += kBatch * kRaceThreads) {
+            float vt[kBatch][4], vd[kBatch][4];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const float4 t4 = load_stream_f4(t4p + j + q * kRaceThreads);
+                vt[q][0] = t4.x; vt[q][1] = t4.y; vt[q][2] = t4.z; vt[q][3] = t4.w;
+                float4 d4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (residual) d4 = load_stream_f4(d4p + j + q * kRaceThreads);
+                vd[q][0] = d4.x; vd[q][1] = d4.y; vd[q][2] = d4.z; vd[q][3] = d4.w;
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) block(j + q * kRaceThreads, vt[q], vd[q]);
+        }
+    }
+    for (; j < j1; j += kRaceThreads) {
         float vt[4], vd[4] = {0.f, 0.f, 0.f, 0.f};
         if (vec) {
             const float4 t4 = load_stream_f4(reinterpret_cast<const float4*>(zt) + j);
@@ -280,21 +368,7 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
                 if (residual) vd[e] = zd[x];
             }
         }
-        philox4x32_10(w0, w1, w2, w3, k0, k1);
-        const uint32_t w[4] = {w0, w1, w2, w3};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int x = 4 * j + e;
-            if (x >= V) break;
-            const float E = -__builtin_amdgcn_logf(philox_uniform(w[e])) * kLn2;
-            const float pt = __builtin_amdgcn_exp2f(fmaf(vt[e], c1, -ct)) * rst;
-            if (pt > 0.f) race_merge(bp, {E * __builtin_amdgcn_rcpf(pt), x});
-            if (residual) {
-                const float pd = __builtin_amdgcn_exp2f(fmaf(vd[e], c1, -cd)) * rsd;
-                const float rr = pt - pd;
-                if (rr > 0.f) race_merge(br, {E * __builtin_amdgcn_rcpf(rr), x});
-            }
-        }
+        block(j, vt, vd);
     }
     for (int o = 32; o > 0; o >>= 1) {
         race_merge(br, {__shfl_xor(br.key, o), __shfl_xor(br.x, o)});
@@ -312,14 +386,40 @@ __global__ __launch_bounds__(kRaceThreads) void accept_race_kernel(AcceptArgs a,
 
 __global__ __launch_bounds__(64) void accept_finalize_kernel(AcceptArgs a, const Decision* dec,
                                                              const RaceKey* race, int nrace) {
-    const int b = blockIdx.x;
-    if (threadIdx.x != 0) return;
+    const int b = blockIdx.x, lane = threadIdx.x;
     RaceKey br{__builtin_huge_valf(), 0x7fffffff}, bp{__builtin_huge_valf(), 0x7fffffff};
-    for (int k = 0; k < nrace; ++k) {
+    for (int k = lane; k < nrace; k += 64) {          // a slice per lane, then across lanes
         race_merge(br, race[((size_t)b * nrace + k) * 2 + 0]);
         race_merge(bp, race[((size_t)b * nrace + k) * 2 + 1]);
     }
-    const int pos = dec[b].pos;
+    for (int o = 32; o > 0; o >>= 1) {
+        race_merge(br, {__shfl_xor(br.key, o), __shfl_xor(br.x, o)});
+        race_merge(bp, {__shfl_xor(bp.key, o), __shfl_xor(bp.x, o)});
+    }
+    const Decision d = dec[b];
+    const int pos = d.pos;
+    if (pos < a.gamma && br.x == 0x7fffffff) {
+        // max(0, p - q) vanished everywhere: the race over p itself (same keys as the race
+        // kernel computes after full acceptance), run here by the whole wave
+        const float* zt = a.target + ((size_t)b * (a.gamma + 1) + pos) * a.V;
+        const float c1 = a.inv_temp * kLog2e;
+        for (int j = lane; 4 * j < a.V; j += 64) {
+            uint32_t w0 = (uint32_t)j, w1 = ((uint32_t)kRaceStream << 16) | (uint32_t)pos,
+                     w2 = (uint32_t)b, w3 = (uint32_t)a.offset;
+            philox4x32_10(w0, w1, w2, w3, (uint32_t)a.seed, (uint32_t)(a.seed >> 32));
+            const uint32_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = 4 * j + e;
+                if (x >= a.V) break;
+                const float E = -__builtin_amdgcn_logf(philox_uniform(w[e])) * kLn2;
+                const float pt = __builtin_amdgcn_exp2f(fmaf(zt[x], c1, -d.ct)) * d.rst;
+                if (pt > 0.f) race_merge(bp, {E * __builtin_amdgcn_rcpf(pt), x});
+            }
+        }
+        for (int o = 32; o > 0; o >>= 1) race_merge(bp, {__shfl_xor(bp.key, o), __shfl_xor(bp.x, o)});
+    }
+    if (lane != 0) return;
     const bool use_r = pos < a.gamma && br.x != 0x7fffffff;
     a.out_tokens[(size_t)b * (a.gamma + 1) + pos] = use_r ? br.x : bp.x;
 }
@@ -352,8 +452,7 @@ hipError_t launch_accept(const AcceptArgs& a, void* ws, hipStream_t s) {
     if (e != hipSuccess) return e;
     accept_decide_kernel<<<a.B, 64, 0, s>>>(a, parts, p.nslice, rows, dec);
     if ((e = hipGetLastError()) != hipSuccess || greedy) return e;
-    accept_race_kernel<<<dim3(p.nrace, a.B), kRaceThreads, 0, s>>>(a, parts, p.nslice, rows, dec,
-                                                                   race, p.nrace);
+    accept_race_kernel<<<dim3(p.nrace, a.B), kRaceThreads, 0, s>>>(a, dec, race, p.nrace);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     accept_finalize_kernel<<<a.B, 64, 0, s>>>(a, dec, race, p.nrace);
     return hipGetLastError();

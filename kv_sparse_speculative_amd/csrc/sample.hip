@@ -45,7 +45,8 @@ __device__ __forceinline__ float sum_merge(float z1, float s1, float z2, float s
 }
 
 // Per-thread state of one slice. Each thread visits its tokens in increasing order, so a later
-// token replaces the best only when strictly better and ties keep the lowest id.
+// token replaces the best only when strictly better and ties keep the lowest id. Only entries
+// above -inf are tracked; a row without one is rescanned by the finalize kernel.
 template <bool SAMPLE, bool STATS>
 struct SliceState {
     float bk = __builtin_huge_valf(), best = kNegInf, s = 0.f;
@@ -171,16 +172,30 @@ __global__ __launch_bounds__(64) void sample_finalize_kernel(SampleArgs a, const
         key_merge(bk, bx, __shfl_xor(bk, o), __shfl_xor(bx, o));
         max_merge(best, bi, best2, __shfl_xor(bi, o));
     }
+    // The argmax is over the non-NaN entries: a row in which no entry exceeds -inf has its
+    // argmax at its first non-NaN entry (-1 if none), found by a scan of the whole wave.
+    int arg = bi;
+    if (bi == 0x7fffffff) {
+        const float* z = a.logits + (size_t)b * a.V;
+        arg = -1;
+        for (int x0 = 0; x0 < a.V; x0 += 64) {          // wave-uniform trip count
+            const int x = x0 + lane;
+            const float v = x < a.V ? z[x] : __builtin_nanf("");
+            int f = v == v ? x : 0x7fffffff;
+            for (int o = 32; o > 0; o >>= 1) f = min(f, __shfl_xor(f, o));
+            if (f != 0x7fffffff) { arg = f; break; }
+        }
+    }
     if (lane != 0) return;
     const bool sample = a.inv_temp != 0.f;
-    a.tokens[b] = sample ? bx : bi;
+    a.tokens[b] = sample ? bx : arg;
     if (a.stats != nullptr) {
         // max of z / t is (max z) / t: rounding is monotone, so the two agree exactly
         float* o = a.stats + (size_t)b * 4;
         o[0] = sample ? best * a.inv_temp : 0.f;
         o[1] = sample ? s : 0.f;
         o[2] = 0.f;
-        o[3] = (float)bi;
+        o[3] = (float)arg;
     }
 }
 

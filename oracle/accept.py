@@ -37,9 +37,13 @@ def softmax(z, temperature):
 
 
 def argmax_lowest(z):
-    """Index of the maximum, the lowest index on ties."""
+    """Index of the maximum over the non-NaN entries, the lowest index on ties; -1 when the row
+    holds no such entry (a reading: the pages take argmax over well-formed logits only)."""
     z = np.asarray(z)
-    return int(np.flatnonzero(z == z.max())[0])
+    ok = ~np.isnan(z)
+    if not ok.any():
+        return -1
+    return int(np.flatnonzero(ok & (z == z[ok].max()))[0])
 
 
 def exponential_race(weights, u):

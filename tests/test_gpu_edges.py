@@ -188,3 +188,38 @@ def test_accept_statistics_rows_written_in_full(gamma):
         np.testing.assert_array_equal(s[:, : gamma + 1, 3].astype(np.int64), z.argmax(axis=2))
         if temp == 0:
             assert (s[:, : gamma + 1, :3] == 0).all() and (s[:, gamma + 1:] == 0).all()
+
+
+def _malformed_rows(B, V, seed):
+    """Logit rows [B, V]: all NaN, all -inf, NaN sprinkled over finite values with a tie at the
+    maximum, then ordinary rows."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    z = torch.randn((B, V), generator=g) * 2.0
+    z[0] = float("nan")
+    z[1] = -float("inf")
+    z[2, ::7] = float("nan")
+    z[2, 11] = z[2, 40] = 50.0
+    return z
+
+
+@pytest.mark.parametrize("V", [1000, 4099])
+def test_greedy_argmax_on_malformed_rows(V):
+    import oracle.accept as oacc
+    B, gamma = 5, 2
+    z = _malformed_rows(B, V, 3)
+    tok, st = kvss.draft_sample(z.cuda(), 0.0, want_stats=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(tok), oacc.draft_sample(z.numpy(), 0.0))
+    assert host(st)[0, 3] == -1.0 and host(tok)[0] == -1
+    # greedy acceptance with those rows as target position 0 (draft tokens equal the argmax
+    # where one exists, so acceptance reaches position 1)
+    t = torch.randn((B, gamma + 1, V)) * 2.0
+    t[:, 0] = z
+    x = torch.from_numpy(np.stack([[max(oacc.argmax_lowest(z[b].numpy()), 0), 3]
+                                   for b in range(B)]).astype(np.int32))
+    out, n, rs = kvss.spec_accept(t.cuda(), None, x.cuda(), 0.0, want_stats=True)
+    torch.cuda.synchronize()
+    r_out, r_n = oacc.greedy_accept(t.numpy(), x.numpy())
+    np.testing.assert_array_equal(host(out), r_out)
+    np.testing.assert_array_equal(host(n), r_n)
+    assert host(rs)[0, 0, 3] == -1.0 and host(out)[0, 0] == -1

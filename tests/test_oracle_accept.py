@@ -184,3 +184,31 @@ def test_draft_stream_is_independent_of_the_acceptance_race():
     u_draft = draft_uniforms(5, 3, 1, 2, 64)
     assert not np.any(u_race == u_draft)
     assert abs(np.corrcoef(u_race, u_draft)[0, 1]) < 0.4
+
+
+def test_argmax_over_non_nan_entries():
+    """Reading of argmax on malformed rows: NaN entries are skipped (lowest index of the maximum
+    of the rest); a row of -inf has its maximum at every entry, so index 0; a row of NaN has no
+    argmax (-1). Brute force over small rows with NaN / -inf / ties placed at every position."""
+    inf = np.inf
+    assert argmax_lowest([-inf] * 5) == 0
+    assert argmax_lowest([np.nan, np.nan]) == -1
+    assert argmax_lowest([1.0, np.nan, 3.0, 3.0]) == 2
+    assert argmax_lowest([np.nan, -inf, -2.0]) == 2
+    rng = np.random.default_rng(7)
+    for _ in range(500):
+        n = int(rng.integers(1, 9))
+        z = rng.choice([-inf, -1.0, 0.0, 2.0, np.nan], size=n)
+        ok = [i for i in range(n) if not math.isnan(z[i])]
+        want = -1 if not ok else min(i for i in ok if z[i] == max(z[j] for j in ok))
+        assert argmax_lowest(z) == want
+
+
+def test_greedy_accept_on_a_row_without_argmax():
+    """A target row of NaN has argmax -1: the draft token there is rejected and -1 emitted."""
+    t = np.zeros((1, 3, 4))
+    t[0, 0, 2] = 5.0
+    t[0, 1, :] = np.nan
+    out, n = greedy_accept(t, np.array([[2, 1]], dtype=np.int32))
+    assert n.tolist() == [1] and out.tolist() == [[2, -1, -1]]
+    assert draft_sample(np.array([[np.nan, np.nan], [-np.inf, -np.inf]]), 0.0).tolist() == [-1, 0]
