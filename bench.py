@@ -30,32 +30,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "kv_sparse_speculative_amd", "csrc", "attn_mf
 COPY_BYTES = 1 << 30          # plain copy used to calibrate the HBM byte counters
 
 
-def source_digest():
-    """Digest of what decides the verify kernel's code and launch: its source, the headers it
-    includes, the planner that splits its key ranges, and the compiler flags."""
-    import hashlib
-    from kv_sparse_speculative_amd import build as kbuild
-    h = hashlib.sha256()
-    csrc = os.path.dirname(KERNEL_SOURCE)
-    for path in (KERNEL_SOURCE, os.path.join(csrc, "common.h"), os.path.join(csrc, "launch.h"),
-                 os.path.join(csrc, "plan.h")):
-        h.update(open(path, "rb").read())
-    h.update(" ".join(kbuild.HIPCC_FLAGS).encode())
-    return h.hexdigest()[:16]
-
-
-def traffic_summary_path(workload):
-    """The committed counter summary of the verify kernel on one workload."""
-    return os.path.join(ROOT, "profiles", f"verify_attn_{workload}_traffic.md")
-
-
 def verify_kernel_name(wl):
     """The verify kernel instance a workload launches (one 16-row tile up to 16 query rows per
-    KV head, else two)."""
+    KV head, else two; up to 8 rows the tile's spare rows carry the lo parts of P)."""
     rows = wl.group * (wl.gamma + 1)
     if wl.dtype != "bf16":
         return f"attn_simple_kernel<{wl.head_dim}, false>"
-    return f"attn_mfma_kernel<{wl.head_dim}, false, {1 if rows <= 16 else 2}>"
+    fold = "true" if rows <= 8 else "false"
+    return f"attn_mfma_kernel<{wl.head_dim}, false, {1 if rows <= 16 else 2}, {fold}>"
 
 
 def verify_algorithmic_bytes(wl):
@@ -66,25 +48,6 @@ def verify_algorithmic_bytes(wl):
     return algorithmic_bytes(wl, P, wl.gamma + 1, 16, 496, wl.vocab)["verify"]
 
 
-def committed_traffic(workload):
-    """HBM bytes per verify launch from the committed counter summary of this workload, if one
-    exists and was taken on the current kernel source; otherwise None."""
-    path = traffic_summary_path(workload)
-    if not os.path.exists(path):
-        return None
-    fields = {}
-    for line in open(path):
-        if line.startswith("- ") and ":" in line:
-            k, v = line[2:].split(":", 1)
-            fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel source sha256/16") != source_digest():
-        return None
-    try:
-        return int(fields["HBM bytes per launch"])
-    except (KeyError, ValueError):
-        return None
-
-
 def _read_csv_rows(directory, suffix):
     import csv
     import glob
@@ -92,64 +55,6 @@ def _read_csv_rows(directory, suffix):
     for f in glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True):
         rows.extend(csv.DictReader(open(f)))
     return rows
-
-
-def summarize_pmc(fetch_dir, write_dir, out_path, command, wl):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the verify kernel and of the calibration
-    copy -> profiles summary with the copy-scaled HBM bytes per verify launch on workload wl."""
-    kernel = verify_kernel_name(wl)
-    algo = verify_algorithmic_bytes(wl)
-    def per_kernel(directory, counter):
-        vals = {}
-        rows = [r for r in _read_csv_rows(directory, "counter_collection.csv")
-                if r.get("Counter_Name") == counter]
-        for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
-    pick = lambda d, key: next((v for k, v in d.items() if key in k), [])
-    # The verify launches are the dispatches of the verify kernel instance that read at least
-    # half its largest read (a T = 1 decode over the compact draft cache can run the same
-    # instance); both runs execute the same program, so the write run's dispatches of that
-    # instance are matched by launch order.
-    kf, kw = pick(fetch, kernel), pick(write, kernel)
-    idx = [i for i, v in enumerate(kf) if v >= 0.5 * max(kf)]
-    vf = [kf[i] for i in idx]
-    vw = [kw[i] for i in idx if i < len(kw)]
-    # calibration copy: torch's device-to-device copy of COPY_BYTES runs as the runtime's blit
-    # kernel; its largest dispatches are the 1 GiB copies
-    cf = [v for k, v in fetch.items() if "copyBuffer" in k]
-    cw = [v for k, v in write.items() if "copyBuffer" in k]
-    cfk = max(max(v) for v in cf) if cf else None
-    cwk = max(max(v) for v in cw) if cw else None
-    f_scale = COPY_BYTES / (cfk * 1024) if cfk else None
-    w_scale = COPY_BYTES / (cwk * 1024) if cwk else None
-    mean = lambda v: sum(v) / len(v)
-    fetch_b = mean(vf) * 1024 * f_scale
-    write_b = mean(vw) * 1024 * w_scale
-    total = int(fetch_b + write_b)
-    lines = [
-        f"# Verify attention on `{wl.name}` (batch {wl.batch}, {wl.num_q_heads} / {wl.num_kv_heads} "
-        f"heads, head_dim {wl.head_dim}, prompts {wl.prompt[0]}-{wl.prompt[1]}, gamma {wl.gamma}): "
-        "HBM traffic",
-        "",
-        "Counter runs (each counter in its own run), then this summary:",
-        "",
-        *[f"    {c}" for c in command],
-        "",
-        f"- kernel: `{kernel}`",
-        f"- kernel source sha256/16: `{source_digest()}`",
-        f"- FETCH_SIZE per dispatch (KiB, mean of {len(vf)}): {mean(vf):.1f}",
-        f"- WRITE_SIZE per dispatch (KiB, mean of {len(vw)}): {mean(vw):.1f}",
-        f"- calibration copy of {COPY_BYTES} B: FETCH_SIZE {cfk:.1f} KiB, WRITE_SIZE {cwk:.1f} KiB",
-        f"- scale factors (bytes / counter bytes): fetch {f_scale:.4f}, write {w_scale:.4f}",
-        f"- HBM bytes per launch: {total}",
-        f"- algorithmic bytes per launch: {algo}",
-        f"- traffic / algorithmic: {total / algo:.4f}",
-    ]
-    open(out_path, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines))
 
 
 def verify_dispatches(stats_dir, wl, warmup):
@@ -202,6 +107,145 @@ def summarize_stats(stats_dir, out_path, title, command, wl=None, warmup=3):
     print("\n".join(lines))
 
 
+def library_digest():
+    """Digest of everything that decides the library's kernels and launches: every source and
+    header, the C ABI header and the compiler flags."""
+    import glob
+    import hashlib
+    from kv_sparse_speculative_amd import build as kbuild
+    h = hashlib.sha256()
+    csrc = os.path.dirname(KERNEL_SOURCE)
+    for path in sorted(glob.glob(os.path.join(csrc, "*"))) + [os.path.join(ROOT, "include", "kvss.h")]:
+        if path.endswith((".hip", ".h")):
+            h.update(os.path.basename(path).encode())
+            h.update(open(path, "rb").read())
+    h.update(" ".join(kbuild.HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+MARK_KERNEL = "philox_kernel"       # the marker launched before every call in --mark-calls runs
+
+
+def _dispatches(directory):
+    """Counter rows of one rocprofv3 run, grouped per dispatch in launch order:
+    [(dispatch id, kernel name, {counter: value})]."""
+    by_id = {}
+    for r in _read_csv_rows(directory, "counter_collection.csv"):
+        d = by_id.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], {}])
+        d[1][r["Counter_Name"]] = d[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [(i, n, c) for i, (n, c) in sorted(by_id.items())]
+
+
+def _short_kernel(name):
+    return (name.replace("void ", "").replace("kvss::(anonymous namespace)::", "")
+            .replace("kvss::", "").split("(")[0])
+
+
+def split_calls(directory, calls):
+    """Per marked call: the dispatches between its marker and the next one. Returns
+    ({call: [segment, ...]}, [calibration-copy dispatches]); a segment is the list of
+    (kernel name, {counter: value}) of one occurrence of the call."""
+    segs, copies, cur = [], [], None
+    for _, name, ctr in _dispatches(directory):
+        if MARK_KERNEL in name:
+            cur = []
+            segs.append(cur)
+        elif "copyBuffer" in name:
+            copies.append(ctr)
+        elif cur is not None and "kvss" in name:
+            cur.append((name, ctr))
+    if len(segs) != len(calls):
+        raise ValueError(f"{directory}: {len(segs)} marked segments for {len(calls)} calls")
+    out = {}
+    for call, seg in zip(calls, segs):
+        out.setdefault(call, []).append(seg)
+    return out, copies
+
+
+def summarize_calls(dirs, calls_path, out_path, command, wl, algo):
+    """Counter summary per call of one marked bench run per directory (each directory one
+    rocprofv3 --pmc pass). FETCH_SIZE and WRITE_SIZE become HBM bytes, each scaled by what the
+    same counter reads for the run's plain 1 GiB copy; every other counter is reported as its
+    mean per call (summed over the call's kernels) and per kernel."""
+    import json as _json
+    calls = _json.load(open(calls_path))
+    mean = lambda v: sum(v) / len(v) if v else 0.0
+    per_call, per_kernel, scale = {}, {}, {}
+    for d in dirs:
+        split, copies = split_calls(d, calls)
+        for counter in sorted({c for segs in split.values() for seg in segs for _, ctr in seg for c in ctr}):
+            if counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                big = max((c.get(counter, 0.0) for c in copies), default=0.0)
+                scale[counter] = COPY_BYTES / (big * 1024) if big > 0 else None
+            for call, segs in split.items():
+                per_call.setdefault(call, {})[counter] = mean(
+                    [sum(ctr.get(counter, 0.0) for _, ctr in seg) for seg in segs])
+                for name, _ in segs[0]:
+                    k = _short_kernel(name)
+                    per_kernel.setdefault(call, {}).setdefault(k, {})[counter] = mean(
+                        [sum(ctr.get(counter, 0.0) for n, ctr in seg if _short_kernel(n) == k)
+                         for seg in segs])
+    lines = [f"# HBM traffic and counters per call on `{wl.name}` (batch {wl.batch}, "
+             f"{wl.num_q_heads} / {wl.num_kv_heads} heads, head_dim {wl.head_dim}, prompts "
+             f"{wl.prompt[0]}-{wl.prompt[1]}, gamma {wl.gamma})", "",
+             "Counter runs (one rocprofv3 --pmc pass each), then this summary:", "",
+             *[f"    {c}" for c in command], "",
+             f"- library sha256/16: `{library_digest()}`",
+             f"- scale factors (bytes per counter byte, from a plain {COPY_BYTES}-byte copy): "
+             f"fetch {scale.get('FETCH_SIZE')}, write {scale.get('WRITE_SIZE')}", ""]
+    have_bytes = scale.get("FETCH_SIZE") and scale.get("WRITE_SIZE")
+    if have_bytes:
+        lines += ["| call | HBM read (B) | HBM write (B) | HBM bytes | algorithmic bytes | traffic / algorithmic |",
+                  "|---|---|---|---|---|---|"]
+        for call in dict.fromkeys(calls):
+            if call == "setup":
+                continue
+            c = per_call[call]
+            rd = int(c.get("FETCH_SIZE", 0.0) * 1024 * scale["FETCH_SIZE"])
+            wr = int(c.get("WRITE_SIZE", 0.0) * 1024 * scale["WRITE_SIZE"])
+            al = algo.get(call)
+            ratio = f"{(rd + wr) / al:.4f}" if al else "-"
+            lines.append(f"| {call} | {rd} | {wr} | {rd + wr} | {al if al else '-'} | {ratio} |")
+        lines.append("")
+    other = sorted({k for c in per_call.values() for k in c} - {"FETCH_SIZE", "WRITE_SIZE"})
+    if other:
+        lines += ["Other counters, mean per call:", "",
+                  "| call | kernel | " + " | ".join(other) + " |", "|---|---|" + "---|" * len(other)]
+        for call in dict.fromkeys(calls):
+            if call == "setup":
+                continue
+            for k, ctr in per_kernel.get(call, {}).items():
+                lines.append(f"| {call} | `{k}` | " + " | ".join(f"{ctr.get(o, 0.0):.4g}" for o in other) + " |")
+        lines.append("")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def calls_summary_path(workload):
+    """The committed per-call traffic summary of one workload."""
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+
+
+def committed_call_traffic(workload):
+    """{call: (HBM bytes, traffic / algorithmic)} from the committed per-call summary of this
+    workload, if it was taken on the current library sources; else {}."""
+    path = calls_summary_path(workload)
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    if f"library sha256/16: `{library_digest()}`" not in text:
+        return {}
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[3].isdigit():
+            try:
+                out[cells[0]] = (int(cells[3]), float(cells[5]))
+            except ValueError:
+                out[cells[0]] = (int(cells[3]), None)
+    return out
+
+
 def algorithmic_bytes(wl, P, T, sink, window, V):
     """Bytes each call must move (inputs read once, outputs written once); per the definitions:
     verify: all K and V rows of every sequence + Q + fp32 O and LSE; draft: the attended K and V
@@ -227,7 +271,7 @@ def algorithmic_bytes(wl, P, T, sink, window, V):
     return out
 
 
-def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
+def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail, mark=None):
     """The calls around the hot path, each timed alone after a scrub read of the K cache (so
     the last-level cache holds none of its bytes):
       kv_append            the gamma + 1 verify rows of every sequence (rewritten in place
@@ -238,11 +282,15 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
       draft_topk_dynamic   one dynamic Top-K draft step (budget - 1 keys searched over the
                            whole prefix, plus the current token), next to the static draft
       draft_sample         the draft token of one draft step from the draft's logits
-                           (temperature 1)."""
+                           (temperature 1).
+    With `mark` (a counter run), each call runs once after mark(name) and the algorithmic bytes
+    per call are returned instead of timings."""
     import numpy as np
     import torch
     from kv_sparse_speculative_amd import kvss
 
+    if mark is not None:
+        mark("setup")                     # the set-up below is not one of the calls
     dev = ns.k_cache.device
     B, Hkv, D, T = ns.batch, wl.num_kv_heads, wl.head_dim, ns.T
     eb = ns.k_cache.element_size()
@@ -304,6 +352,11 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail):
               "draft_snapkv_compact": n_rows * row + q_out,
               "draft_topk_dynamic": prefix_k + dyn_rows * row + q_out,
               "draft_sample": q_logits.numel() * 4 + B * 4}
+    if mark is not None:
+        for name, fn in calls.items():
+            mark(name)
+            fn()
+        return nbytes
     out = {}
     for name, fn in calls.items():
         times = []
@@ -468,14 +521,26 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after timing, run a plain 1 GiB copy (counter calibration)")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "OUT"))
+    ap.add_argument("--mark-calls", metavar="JSON",
+                    help="counter-run mode: after warm-up, run the steps and the f-row calls once "
+                         "each with a marker kernel before every call, write the call order and "
+                         "algorithmic bytes to JSON, and print no benchmark line")
+    ap.add_argument("--summarize-calls", nargs="+", metavar="ARG",
+                    help="CALLS_JSON OUT DIR [DIR ...]: per-call summary of marked counter runs")
     ap.add_argument("--title", default="kvss kernels")
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
-    if args.summarize_pmc:
+    if args.summarize_calls:
         from kv_sparse_speculative_amd.workloads import HEADLINE, WORKLOADS
-        summarize_pmc(*args.summarize_pmc, args.command, WORKLOADS[args.workload or HEADLINE])
+        calls_json, out, *dirs = args.summarize_calls
+        import json as _json
+        meta = _json.load(open(calls_json))
+        tmp = calls_json + ".order"
+        _json.dump(meta["calls"], open(tmp, "w"))
+        summarize_calls(dirs, tmp, out, args.command, WORKLOADS[args.workload or HEADLINE],
+                        meta["algorithmic"])
+        os.remove(tmp)
         return
     if args.summarize_stats:
         from kv_sparse_speculative_amd.workloads import HEADLINE, WORKLOADS
@@ -530,10 +595,12 @@ def main():
     calls = ["snapkv_select", "streaming_set", "verify", "draft_streaming", "spec_accept", "draft_snapkv"]
     state = {}
 
-    def step(ev=None):
+    def step(ev=None, marker=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
+            if marker is not None and i < len(calls):
+                marker(calls[i])
         mark(0)
         kvss.snapkv_select(kv_p, ns.q_obs, w, pool, budget, sel_idx=sel, sel_count=cnt,
                            workspace=snap_ws)
@@ -559,6 +626,29 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.mark_calls:
+        # Counter run: a one-counter Philox launch (a kernel the path never launches) before
+        # every call splits the dispatch stream into calls.
+        ctr = torch.zeros((1, 4), dtype=torch.int32, device=dev)
+        ctr_out = torch.empty_like(ctr)
+        order = []
+
+        def marker(name):
+            kvss.kvss_philox4x32_10(ctr, 0, out=ctr_out)
+            order.append(name)
+        for _ in range(args.steps):
+            step(marker=marker)
+        nb = algorithmic_bytes(wl, P, T, sink, window, ns.vocab)
+        nb.update(measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, 1, None, mark=marker))
+        if args.copy_reference:
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(2):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        json.dump({"calls": order, "algorithmic": nb}, open(args.mark_calls, "w"))
+        print(f"marked {len(order)} calls -> {args.mark_calls}", flush=True)
+        return
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -606,6 +696,7 @@ def main():
     small_gbs = small / (rd[2] * 1e-3) / 1e9
 
     total_bytes = sum(nbytes.values())
+    traffic = committed_call_traffic(wl.name)
     detail = {}
     for c in calls:
         ms = per_call[c]
@@ -617,6 +708,8 @@ def main():
         if c.startswith("draft"):
             d["tokens_per_s"] = round(B / (ms * 1e-3), 1)
             d["frac_stream_same_size"] = round(gbs / small_gbs, 4)
+        if c in traffic:
+            d["traffic_ratio"] = traffic[c][1]
         detail[c] = d
     v = detail["verify"]
     result = {
@@ -636,7 +729,7 @@ def main():
                    "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": D,
                    "snapkv_budget": budget, "streaming": [sink, window], "vocab": ns.vocab},
         "roofline": {"bound": "hbm", "achieved": v["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": v["frac_peak"], "traffic": committed_traffic(wl.name),
+                     "frac": v["frac_peak"], "traffic": traffic.get("verify", (None,))[0],
                      "kernel": "verify_attn_full"},
         "calls": detail,
         "stream_read_GB_per_s": round(stream_gbs, 1),
@@ -644,6 +737,9 @@ def main():
     }
     result["next"] = measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, args.steps,
                                                detail["draft_snapkv"])
+    for name, d in result["next"].items():
+        if name in traffic:
+            d["traffic_ratio"] = traffic[name][1]
     if wl.name.startswith("llama8b"):
         from kv_sparse_speculative_amd import speedup_model
         rates = speedup_model.rates_from_bench(detail, result["next"], stream_gbs, B, maxP,

@@ -1,8 +1,9 @@
-"""CPU checks of bench.py's profile tooling on fabricated rocprofv3 CSVs: the verify dispatches
-are told apart from a compact-cache decode of the same kernel instance (same grid, smaller
-read) and matched between the two counter runs by launch order; the copy calibration scales
-the counters; the kernel-trace summary averages only the timed steps' verify calls and the
-merges that follow them; and a summary is trusted only for its own workload."""
+"""CPU checks of bench.py's profile tooling on fabricated rocprofv3 CSVs: a marked counter run is
+split into calls at the marker kernel (kernels outside the library and the set-up segment are
+dropped, repeated calls are averaged, a marker-count mismatch is an error); the copy
+calibration scales the byte counters; the kernel-trace summary averages only the timed steps'
+verify calls and the merges that follow them; and a summary is trusted only for its own
+workload."""
 
 import csv
 import os
@@ -29,28 +30,54 @@ def _counters(directory, counter, values):
     _write(os.path.join(directory, "run", "x_counter_collection.csv"), header, rows)
 
 
-def test_pmc_summary_picks_the_verify_dispatches(tmp_path):
-    algo = bench.verify_algorithmic_bytes(WL)
-    fetch_kib = algo / 2 / 1024            # FETCH_SIZE counts half the bytes (copy scale 2.0)
-    copy = bench.COPY_BYTES / 1024
-    # verify, compact decode (same kernel instance and grid, small read), verify, a copy, verify
-    _counters(str(tmp_path / "f"), "FETCH_SIZE", [
-        (65536, KERNEL, fetch_kib), (65536, KERNEL, fetch_kib / 16), (65536, KERNEL, fetch_kib),
-        (512, "__amd_rocclr_copyBuffer", copy / 2), (65536, KERNEL, fetch_kib)])
-    _counters(str(tmp_path / "w"), "WRITE_SIZE", [
-        (65536, KERNEL, 100.0), (65536, KERNEL, 7.0), (65536, KERNEL, 100.0),
-        (512, "__amd_rocclr_copyBuffer", copy), (65536, KERNEL, 100.0)])
-    out = tmp_path / "summary.md"
-    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), str(out), ["cmd"], WL)
-    fields = {}
+def _marked_run(directory, counter, seq):
+    """seq: list of (kernel name, value) in launch order; Dispatch_Id follows the order."""
+    _counters(directory, counter, [(256, k, v) for k, v in seq])
+
+
+def test_call_summary_splits_at_markers_and_scales_by_the_copy(tmp_path):
+    mark = "kvss::(anonymous namespace)::philox_kernel(HIP_vector_type<unsigned int, 4u> const*)"
+    rs = "void kvss::(anonymous namespace)::snap_rowstats_mfma<128, 8, false>(kvss::SnapArgs)"
+    cs = "void kvss::(anonymous namespace)::snap_colscore_mfma<128, 8>(kvss::SnapArgs)"
+    vk = f"void kvss::(anonymous namespace)::{KERNEL}(kvss::AttnArgs)"
+    mg = "kvss::(anonymous namespace)::merge_kernel(float const*, int, int, float*, float*)"
+    copy = "__amd_rocclr_copyBuffer"
+    calls = ["snapkv_select", "verify", "snapkv_select", "verify", "setup", "kv_append"]
+    fetch = [(mark, 0.0), (rs, 100.0), (cs, 100.0), (mark, 0.0), (vk, 400.0), (mg, 4.0),
+             (mark, 0.0), (rs, 110.0), (cs, 90.0), (mark, 0.0), (vk, 400.0), (mg, 4.0),
+             (mark, 0.0), ("void at::native::index_kernel(int)", 9.0), (mark, 0.0),
+             ("kvss::(anonymous namespace)::kv_append_kernel(kvss::AppendArgs)", 3.0),
+             (copy, bench.COPY_BYTES / 1024 / 2)]        # FETCH_SIZE reads half a copy
+    write = [(k, 1.0 if k != copy else bench.COPY_BYTES / 1024) for k, _ in fetch]
+    _marked_run(str(tmp_path / "f"), "FETCH_SIZE", fetch)
+    _marked_run(str(tmp_path / "w"), "WRITE_SIZE", write)
+    meta = tmp_path / "calls.json"
+    import json
+    json.dump(calls, open(meta, "w"))
+    algo = {"snapkv_select": 200 * 2 * 1024, "verify": 808 * 1024, "kv_append": 6 * 1024}
+    out = tmp_path / "traffic.md"
+    bench.summarize_calls([str(tmp_path / "f"), str(tmp_path / "w")], str(meta), str(out),
+                          ["cmd"], WL, algo)
+    rows = {}
     for line in open(out):
-        if line.startswith("- ") and ":" in line:
-            k, v = line[2:].split(":", 1)
-            fields[k.strip()] = v.strip()
-    assert fields["FETCH_SIZE per dispatch (KiB, mean of 3)"] == f"{fetch_kib:.1f}"
-    assert fields["WRITE_SIZE per dispatch (KiB, mean of 3)"] == "100.0"
-    assert int(fields["HBM bytes per launch"]) == int(algo + 100 * 1024)
-    assert fields["algorithmic bytes per launch"] == str(algo)
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[3].isdigit():
+            rows[cells[0]] = cells
+    assert "setup" not in rows                      # set-up kernels are not a call
+    # snapkv_select: mean of (100 + 100) and (110 + 90) KiB fetched at scale 2, 2 kernels x 1 KiB written
+    assert int(rows["snapkv_select"][1]) == 200 * 1024 * 2
+    assert int(rows["snapkv_select"][2]) == 2 * 1024
+    assert float(rows["snapkv_select"][5]) == round((400 * 1024 + 2048) / (400 * 1024), 4)
+    assert int(rows["verify"][3]) == 404 * 1024 * 2 + 2 * 1024
+    assert int(rows["kv_append"][3]) == 3 * 1024 * 2 + 1024     # the index kernel is dropped
+
+
+def test_call_summary_rejects_a_marker_count_mismatch(tmp_path):
+    import pytest
+    mark = "kvss::(anonymous namespace)::philox_kernel(x)"
+    _marked_run(str(tmp_path / "f"), "FETCH_SIZE", [(mark, 0.0), ("kvss::a(x)", 1.0)])
+    with pytest.raises(ValueError):
+        bench.split_calls(str(tmp_path / "f"), ["verify", "draft_snapkv"])
 
 
 def test_trace_summary_averages_the_timed_verify_calls(tmp_path):
@@ -73,8 +100,8 @@ def test_trace_summary_averages_the_timed_verify_calls(tmp_path):
     assert merge == [10.0, 10.0, 10.0]
 
 
-def test_committed_traffic_is_per_workload():
+def test_committed_traffic_is_per_workload_and_source():
     # a workload with no committed counter summary reports no traffic
-    assert bench.committed_traffic("tiny_fp32") is None
-    assert bench.traffic_summary_path("llama8b_ctx32k").endswith(
-        os.path.join("profiles", "verify_attn_llama8b_ctx32k_traffic.md"))
+    assert bench.committed_call_traffic("tiny_fp32") == {}
+    assert bench.calls_summary_path("llama8b_ctx32k").endswith(
+        os.path.join("profiles", "traffic_llama8b_ctx32k.md"))
