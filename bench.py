@@ -282,7 +282,9 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail, m
       draft_topk_dynamic   one dynamic Top-K draft step (budget - 1 keys searched over the
                            whole prefix, plus the current token), next to the static draft
       draft_sample         the draft token of one draft step from the draft's logits
-                           (temperature 1).
+                           (temperature 1)
+      decode_full          one decode token per sequence over the whole cache (verify_attn_full
+                           with T = 1): the target's attention step T_T of the speedup model.
     With `mark` (a counter run), each call runs once after mark(name) and the algorithmic bytes
     per call are returned instead of timings."""
     import numpy as np
@@ -319,6 +321,8 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail, m
     o1 = torch.empty((B, wl.num_q_heads, 1, D), dtype=torch.float32, device=dev)
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
 
+    kv_full = kv_p.with_lens(ns.kv_lens_draft, int(P.max()) + 1)
+    o_full = torch.empty((B, wl.num_q_heads, 1, D), dtype=torch.float32, device=dev)
     q_logits = ns.draft_logits[:, 0].contiguous()                     # the draft's logits [B, V]
     d_tok = torch.empty(B, dtype=torch.int32, device=dev)
     ws_s = torch.empty(kvss.lib().kvss_sample_workspace_bytes(B, q_logits.shape[1]),
@@ -338,6 +342,8 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail, m
                                                            want_lse=False, workspace=ws_t),
         "draft_sample": lambda: kvss.draft_sample(q_logits, 1.0, seed=99, offset=1, step=0,
                                                   tokens=d_tok, workspace=ws_s),
+        "decode_full": lambda: kvss.verify_attn_full(kv_full, q1, out=o_full, want_lse=False,
+                                                     workspace=ws),
     }
     calls["draft_cache_build"]()
     torch.cuda.synchronize()
@@ -351,7 +357,8 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail, m
               "draft_cache_build": 2 * n_rows * row + B * Hkv * k * 4,
               "draft_snapkv_compact": n_rows * row + q_out,
               "draft_topk_dynamic": prefix_k + dyn_rows * row + q_out,
-              "draft_sample": q_logits.numel() * 4 + B * 4}
+              "draft_sample": q_logits.numel() * 4 + B * 4,
+              "decode_full": int((P + 1).sum()) * row + q_out}
     if mark is not None:
         for name, fn in calls.items():
             mark(name)
@@ -380,9 +387,91 @@ def measure_next_rows(wl, ns, kv_p, kv_d, sel, cnt, tail, reps, gather_detail, m
     out["draft_round"] = draft_round_timing(wl, ns, kv_d, sel, cnt, tail, q_logits, d_tok, ws_s,
                                             max(reps, 3))
     out["draft_topk_dynamic"]["tokens_per_s"] = round(B / (out["draft_topk_dynamic"]["ms"] * 1e-3), 1)
+    out["decode_full"]["tokens_per_s"] = round(B / (out["decode_full"]["ms"] * 1e-3), 1)
     out["draft_topk_dynamic"]["cost_vs_static_draft"] = round(
         out["draft_topk_dynamic"]["ms"] / gather_detail["ms"], 1)
     return out
+
+
+def measure_config(name, reps, scrub):
+    """One other workload, timed in the same run: the calls it names (verify, SnapKV selection,
+    the SnapKV draft, acceptance with sampling at temperature 1, and the StreamingLLM set and
+    draft where the workload has one), each after a scrub read of `scrub` (more than the 256 MB
+    last-level cache), median of `reps` event-timed calls. Inputs are freed afterwards."""
+    import torch
+    from kv_sparse_speculative_amd import kvss
+    from kv_sparse_speculative_amd.synth import generate
+    from kv_sparse_speculative_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[name]
+    dev = scrub.device
+    ns = generate(wl, device=dev)
+    P = ns.prompt_lens_np
+    B, T, D, Hq, Hkv = ns.batch, ns.T, wl.head_dim, wl.num_q_heads, wl.num_kv_heads
+    budget, w, pool = wl.snapkv
+    sink, window = wl.streaming or (0, 0)
+    maxP = int(P.max())
+    kv_p = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.prompt_lens, maxP)
+    kv_d = kv_p.with_lens(ns.kv_lens_draft, maxP + 1)
+    kv_v = kv_p.with_lens(ns.kv_lens_verify, maxP + T)
+    tail = (ns.prompt_lens - w).contiguous()
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_v = torch.empty((B, Hq, T, D), **f32)
+    l_v = torch.empty((B, Hq, T), **f32)
+    o_d = torch.empty((B, Hq, D), **f32)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sel, cnt, _ = kvss.snapkv_select(kv_p, ns.q_obs, w, pool, budget, workspace=ws)
+    acc_tok = torch.empty((B, T), dtype=torch.int32, device=dev)
+    acc_n = torch.empty(B, dtype=torch.int32, device=dev)
+    calls = {
+        "snapkv_select": lambda: kvss.snapkv_select(kv_p, ns.q_obs, w, pool, budget, sel_idx=sel,
+                                                    sel_count=cnt, workspace=ws),
+        "verify": lambda: kvss.verify_attn_full(kv_v, ns.q_verify, out=o_v, lse=l_v, workspace=ws),
+        "draft_snapkv": lambda: kvss.draft_attn_sparse(kv_d, ns.q_draft, sel, cnt, tail, w + 1,
+                                                       out=o_d, want_lse=False, workspace=ws),
+        "spec_accept": lambda: kvss.spec_accept(ns.target_logits, ns.draft_logits,
+                                                ns.draft_tokens, 1.0, seed=5, offset=2,
+                                                out_tokens=acc_tok, num_accepted=acc_n,
+                                                workspace=ws),
+    }
+    if wl.streaming:
+        s_idx, s_cnt, s_tail = kvss.kvss_streaming_set(ns.kv_lens_draft, Hkv, sink, window)
+        calls["draft_streaming"] = lambda: kvss.draft_attn_sparse(
+            kv_d, ns.q_draft, s_idx, s_cnt, s_tail, window, out=o_d, want_lse=False, workspace=ws)
+    nbytes = algorithmic_bytes(wl, P, T, max(sink, 1), window, ns.vocab)
+    sink_buf = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for c, fn in calls.items():
+        fn()
+        t = []
+        for _ in range(reps):
+            kvss.kvss_stream_read(scrub, sink_buf)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        t.sort()
+        ms = t[len(t) // 2]
+        gbs = nbytes[c] / (ms * 1e-3) / 1e9
+        d = {"ms": round(ms, 4), "GB_per_s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4),
+             "bytes": nbytes[c]}
+        if c == "verify":
+            d["tokens_per_s"] = round(B * T / (ms * 1e-3), 1)
+        if c.startswith("draft"):
+            d["tokens_per_s"] = round(B / (ms * 1e-3), 1)
+        out[c] = d
+    shape = {"batch": B, "context": [int(P.min()), maxP], "gamma": ns.gamma, "q_heads": Hq,
+             "kv_heads": Hkv, "head_dim": D, "dtype": wl.dtype, "snapkv_budget": budget,
+             "vocab": ns.vocab, "reps": reps}
+    if wl.streaming:
+        shape["streaming"] = [sink, window]
+    del ns, kv_p, kv_d, kv_v, ws, calls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"shape": shape, "calls": out}
 
 
 def draft_round_timing(wl, ns, kv_d, sel, cnt, tail, q_logits, tokens, ws_s, reps):
@@ -519,6 +608,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the timing of the other workloads (section 'configs')")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after timing, run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "OUT"))
@@ -745,6 +836,10 @@ def main():
         rates = speedup_model.rates_from_bench(detail, result["next"], stream_gbs, B, maxP,
                                                sink + window)
         result["model"] = speedup_model.summary(rates, B, maxP)
+    if not args.no_other_configs:
+        # every other workload, timed in the same run (its calls alone, cold, median of 5)
+        result["configs"] = {n: measure_config(n, 5, ns.k_cache) for n in WORKLOADS
+                             if n != wl.name}
     if args.copy_reference:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

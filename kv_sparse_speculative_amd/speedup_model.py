@@ -14,8 +14,14 @@ cost stays flat, so the speedup grows with batch size above a critical length S_
 Per-layer times are a roofline of two terms for n query tokens per sequence and R cached rows:
   linear layers  max(weight bytes / read bandwidth, 2 * params * B * n / matrix-core rate)
   attention      B * R * (KV bytes per row) / attention bandwidth  (+ the measured fixed part)
-The attention bandwidths and per-call times come from bench.py's measurements on the GPU; the
-weight read uses the measured stream-read rate; the linear-layer compute uses the dense bf16
+The attention bandwidths come from bench.py's measurements on the GPU, one per call:
+  T_T  a one-token decode over the whole cache (verify_attn_full with T = 1),
+  T_V  the gamma + 1 token verify over the whole cache,
+  T_D  the draft: its measured time at the measured (B, K), of which the part proportional to
+       B * K runs at the decode rate and the rest is a fixed launch cost,
+  T_select (dynamic Top-K) the search over the prefix, timed as the dynamic step minus the
+       static draft.
+The weight read uses the measured stream-read rate; the linear-layer compute uses the dense bf16
 matrix-core peak (an optimistic bound, which favours the target at large batch). alpha cannot
 be measured without trained weights and data, so it is swept.
 """
@@ -44,18 +50,37 @@ def omega(gamma, alpha):
     return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
 
 
+def alpha_from_omega(gamma, om, tol=1e-13):
+    """alpha with omega(gamma, alpha) = om (Eq. (1) increases with alpha), om in [1, gamma + 1]."""
+    if not 1.0 <= om <= gamma + 1.0:
+        raise ValueError(f"Omega {om} outside [1, {gamma + 1}]")
+    lo, hi = 0.0, 1.0
+    while hi - lo > tol:
+        mid = 0.5 * (lo + hi)
+        if omega(gamma, mid) < om:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def sd_time_per_token(gamma_t_draft, t_verify, om):
+    """T_avg^SD = (gamma * T_D + T_V) / Omega (Section 3.1, the text before Eq. (2))."""
+    return (gamma_t_draft + t_verify) / om
+
+
 def sd_cost_ratio(gamma, alpha, t_draft, t_verify, t_target):
     """Eq. (2): T_avg^SD / T_T (speedup is its reciprocal)."""
-    return (gamma * t_draft + t_verify) / (omega(gamma, alpha) * t_target)
+    return sd_time_per_token(gamma * t_draft, t_verify, omega(gamma, alpha)) / t_target
 
 
 class LayerModel:
     """Per-layer step times at batch B and context S from the measured rates.
 
-    rates: attn_verify_Bps (verify attention bandwidth at large reads), attn_draft_Bps (draft
-    attention bandwidth), stream_Bps (plain read rate, used for weights), draft_fixed_s (the
-    measured draft launch's time not explained by its bytes), select_dynamic_Bps (the dynamic
-    Top-K search's bandwidth over the whole prefix).
+    rates: attn_decode_Bps (one-token decode over the whole cache), attn_verify_Bps (gamma + 1
+    token verify), attn_draft_Bps (the draft's per-row rate), draft_fixed_s (the measured draft
+    launch's time not explained by its bytes at that rate), stream_Bps (plain read rate, used
+    for weights), select_dynamic_Bps (the dynamic Top-K search's bandwidth over the prefix).
     """
 
     def __init__(self, arch, rates, bytes_per_elem=2):
@@ -71,7 +96,7 @@ class LayerModel:
 
     def target(self, B, S):
         """T_T: one decode token per sequence over S + 1 rows."""
-        return self.linear(B, 1) + B * (S + 1) * self.row / self.rates["attn_verify_Bps"]
+        return self.linear(B, 1) + B * (S + 1) * self.row / self.rates["attn_decode_Bps"]
 
     def verify(self, B, S, gamma):
         """T_V(gamma): gamma + 1 tokens per sequence over S + gamma + 1 rows (one KV read)."""
@@ -112,19 +137,24 @@ def s_inflection(model, K, alpha, batches=(16, 256), lengths=None):
 
 
 def rates_from_bench(calls, nxt, stream_gbs, wl_batch, wl_context, draft_rows):
-    """Measured rates from bench.py's per-call results (bytes and ms) at one workload."""
+    """Measured rates from bench.py's per-call results (bytes and ms) at one workload: the
+    decode rate from the one-token decode over the whole cache, the verify rate from the verify
+    call, the draft as its measured time split into a part proportional to its rows (at the
+    decode rate) and a fixed remainder, the dynamic search from the dynamic Top-K step."""
     verify = calls["verify"]
-    draft = calls["draft_streaming"]
+    draft = calls["draft_snapkv"]
     attn_verify = verify["bytes"] / (verify["ms"] * 1e-3)
-    # split the measured draft time into a byte-proportional part at the verify-stream rate and
-    # a fixed remainder (launch ramp, prologue, drain)
+    dec = nxt.get("decode_full") if nxt else None
+    attn_decode = dec["bytes"] / (dec["ms"] * 1e-3) if dec else attn_verify
     draft_s = draft["ms"] * 1e-3
-    fixed = max(draft_s - draft["bytes"] / attn_verify, 0.0)
+    fixed = max(draft_s - draft["bytes"] / attn_decode, 0.0)
     rates = {
+        "attn_decode_Bps": attn_decode,
         "attn_verify_Bps": attn_verify,
-        "attn_draft_Bps": attn_verify,
+        "attn_draft_Bps": attn_decode,
         "draft_fixed_s": fixed,
         "stream_Bps": stream_gbs * 1e9,
+        "draft_measured_Bps": draft["bytes"] / draft_s,
     }
     dyn = nxt.get("draft_topk_dynamic") if nxt else None
     if dyn:
@@ -137,17 +167,35 @@ def rates_from_bench(calls, nxt, stream_gbs, wl_batch, wl_context, draft_rows):
     return rates
 
 
+def curves(model, K, alphas, batches=(16, 32, 64, 128, 256),
+           lengths=(1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072), dynamic=False):
+    """Speedup against context length per batch size (Section 3.2, Figs. 2-3 style): for each
+    alpha, {B: [[S, gamma_opt, speedup], ...]}."""
+    out = {}
+    for a in alphas:
+        out[str(a)] = {str(B): [[S, *[round(v, 3) if isinstance(v, float) else v
+                                      for v in best_gamma(model, B, S, K, a, dynamic=dynamic)]]
+                                for S in lengths]
+                       for B in batches}
+    return out
+
+
 def summary(rates, B, S, K_static=512, alphas=(0.6, 0.7, 0.8, 0.9, 0.95)):
-    """The model at the measured point, per strategy and alpha, plus S_inflection."""
+    """The model at the measured point, per strategy and alpha; speedup-vs-S curves per batch
+    size; S_inflection per alpha, and its sensitivity to taking T_T at the verify rate instead
+    of the measured decode rate."""
     m = LayerModel(LLAMA8B_LAYER, rates)
     out = {
         "per_layer_us": {
             "T_T": round(m.target(B, S) * 1e6, 1),
             "T_V_gamma4": round(m.verify(B, S, 4) * 1e6, 1),
+            "T_V_over_T_T": round(m.verify(B, S, 4) / m.target(B, S), 4),
             "T_D_static_K512": round(m.draft(B, K_static) * 1e6, 1),
             "T_select_dynamic": round(m.select_dynamic(B, S) * 1e6, 1),
             "weights_read": round(m.w_bytes / rates["stream_Bps"] * 1e6, 1),
         },
+        "rates_GBps": {k[:-4]: round(v / 1e9, 1) for k, v in rates.items() if k.endswith("_Bps")},
+        "draft_fixed_us": round(rates["draft_fixed_s"] * 1e6, 2),
         "speedup": {},
     }
     for name, dyn in (("static_K512", False), ("dynamic_topk_K512", True)):
@@ -156,5 +204,10 @@ def summary(rates, B, S, K_static=512, alphas=(0.6, 0.7, 0.8, 0.9, 0.95)):
                      round(best_gamma(m, B, S, K_static, a, dynamic=dyn)[1], 3)]
             for a in alphas
         }
-    out["S_inflection_alpha0.8_K512"] = s_inflection(m, K_static, 0.8)
+    out["curves_static_K512"] = curves(m, K_static, (0.7, 0.8, 0.9))
+    alt = LayerModel(LLAMA8B_LAYER, dict(rates, attn_decode_Bps=rates["attn_verify_Bps"]))
+    out["S_inflection_K512"] = {
+        str(a): {"measured_T_T": s_inflection(m, K_static, a),
+                 "T_T_at_verify_rate": s_inflection(alt, K_static, a)}
+        for a in (0.7, 0.8, 0.9)}
     return out
