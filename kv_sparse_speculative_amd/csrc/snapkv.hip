@@ -172,10 +172,67 @@ __device__ int block_scan_1024(int v, int* sh, int& total) {
     return base + x - v;
 }
 
+// Adds one to bin `bin` of `hist` for every lane with `match`: eight ballots give each lane the
+// set of lanes holding the same digit and the lowest of them adds the set's size, one LDS atomic
+// per distinct digit of the wave (one head's scores share a few exponents, so plain atomics would
+// serialise on one bin). Every lane of the wave must call it.
+__device__ __forceinline__ void hist_add_wave(unsigned* hist, unsigned bin, bool match, int lane) {
+    unsigned long long peers = __ballot(match);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const bool set = (bin >> bit) & 1u;
+        const unsigned long long m = __ballot(set);
+        peers &= set ? m : ~m;
+    }
+    if (match && __ffsll((long long)peers) - 1 == lane)
+        atomicAdd(&hist[bin], (unsigned)__popcll(peers));
+}
+
+// Radix select (most significant byte first) by the whole block of the k-th largest of the
+// values its threads offer through count(prefix, mask, shift, hist), which histograms the digit
+// at `shift` of the offered values whose masked bits equal `prefix`. Returns the k-th largest bit
+// pattern; `remaining` becomes how many of the values equal to it belong to the k largest.
+template <typename CountFn>
+__device__ unsigned radix_select_block(unsigned k, unsigned* hist, int* sh, unsigned* s_digit,
+                                       unsigned* s_remaining, unsigned& remaining, CountFn count) {
+    const int tid = threadIdx.x;
+    unsigned prefix = 0, mask = 0;
+    remaining = k;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        count(prefix, mask, shift, hist);
+        __syncthreads();
+        // the bin where the count from the top first reaches `remaining`
+        const int cnt = tid < 256 ? (int)hist[255 - tid] : 0;
+        int tot;
+        const int above = block_scan_1024(cnt, sh, tot);
+        if (tid < 256 && above < (int)remaining && above + cnt >= (int)remaining) {
+            *s_digit = 255 - tid;
+            *s_remaining = remaining - above;
+        }
+        __syncthreads();
+        prefix |= *s_digit << shift;
+        mask |= 255u << shift;
+        remaining = *s_remaining;
+        __syncthreads();
+    }
+    return prefix;
+}
+
+// Prefilter of the generic top-k: candidates held in LDS (bit pattern and position), and the
+// number of position groups whose maxima bound the selection from below.
+constexpr int kPreCap = 7680;      // 60 KB: the static LDS stays within the default 64 KB
+constexpr int kPreGroups = 8192;
+
 __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     __shared__ unsigned hist[256];
     __shared__ int sh[16];
     __shared__ unsigned s_digit, s_remaining;
+    __shared__ unsigned cand_v[kPreCap];
+    __shared__ int cand_j[kPreCap];
+    __shared__ int wcnt[16];
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
     const int n = max(P - a.w, 0);
@@ -192,6 +249,10 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     // Every loop below issues a batch of independent loads before using any (the pooled array
     // is re-read from L2 on every pass; one load at a time would wait out its latency each).
     constexpr int kBatch = 8;
+    static_assert(kBatch * 1024 == kPreGroups, "group j mod kPreGroups is slot q of thread j % 1024");
+    unsigned gmax[kBatch];       // maximum pooled bit pattern of this thread's groups
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) gmax[q] = 0u;
     for (int j0 = tid; j0 < n; j0 += kBatch * 1024) {
         float m[kBatch];
 #pragma unroll
@@ -211,63 +272,125 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
             const int j = j0 + q * 1024;
-            if (j < n) pl[j] = __float_as_uint(m[q]);
+            if (j < n) {
+                pl[j] = __float_as_uint(m[q]);
+                gmax[q] = max(gmax[q], __float_as_uint(m[q]));
+            }
         }
     }
     __syncthreads();
 
-    // Radix select (most significant byte first) of the k-th largest bit pattern. Scores of
-    // one head share a few exponent values, so histogram increments are aggregated per wave:
-    // eight ballots give every lane the set of lanes holding the same digit, and the lowest of
-    // them adds the set's size -- one conflict-free LDS atomic per distinct digit.
-    const int lane = tid & 63;
-    unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
-    const int n_pad = (n + 1023) / 1024 * 1024;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int t = tid; t < 256; t += 1024) hist[t] = 0;
-        __syncthreads();
-        for (int j0 = tid; j0 < n_pad; j0 += kBatch * 1024) {
+    // Prefilter. The positions fall into kPreGroups groups (j mod kPreGroups); the k-th largest
+    // group maximum t0 is reached by at least k pooled values, so every value kept is >= t0.
+    // When the values >= t0 fit in LDS they are compacted there in position order and the
+    // selection runs over them alone; otherwise it runs over the whole pooled array below.
+    if (k <= kPreGroups / 2) {
+        const int lane = tid & 63, wid = tid >> 6;
+        unsigned rem0;
+        const unsigned t0 = radix_select_block(
+            (unsigned)k, hist, sh, &s_digit, &s_remaining, rem0,
+            [&](unsigned prefix, unsigned mask, int shift, unsigned* h) {
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q)
+                    hist_add_wave(h, (gmax[q] >> shift) & 255u, (gmax[q] & mask) == prefix, lane);
+            });
+        // each wave takes one contiguous span of positions (a multiple of 64): count, then place
+        const int span = (n + 16 * 64 - 1) / (16 * 64) * 64;
+        const int w_lo = min(n, wid * span), w_hi = min(n, w_lo + span);
+        int cnt = 0;
+        for (int j0 = w_lo; j0 < w_hi; j0 += kBatch * 64) {
             unsigned uu[kBatch];
 #pragma unroll
             for (int q = 0; q < kBatch; ++q) {
-                const int j = j0 + q * 1024;
-                uu[q] = j < n ? pl[j] : 0u;
+                const int j = j0 + q * 64 + lane;
+                uu[q] = j < w_hi ? pl[j] : 0u;
             }
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int j = j0 + q * 1024;
-                if (j0 - tid + q * 1024 >= n_pad) break;      // uniform: whole 1024-blocks
-                const unsigned u = uu[q];
-                const bool match = j < n && (u & mask) == prefix;
-                const unsigned bin = (u >> shift) & 255u;
-                unsigned long long peers = __ballot(match);
+            for (int q = 0; q < kBatch; ++q)
+                cnt += __popcll(__ballot(j0 + q * 64 + lane < w_hi && uu[q] >= t0));
+        }
+        if (lane == 0) wcnt[wid] = cnt;
+        __syncthreads();
+        int off = 0, total = 0;
+        for (int w2 = 0; w2 < 16; ++w2) {
+            off += w2 < wid ? wcnt[w2] : 0;
+            total += wcnt[w2];
+        }
+        if (total <= kPreCap) {
+            for (int j0 = w_lo; j0 < w_hi; j0 += kBatch * 64) {
+                unsigned uu[kBatch];
 #pragma unroll
-                for (int bit = 0; bit < 8; ++bit) {
-                    const bool set = (bin >> bit) & 1u;
-                    const unsigned long long m = __ballot(set);
-                    peers &= set ? m : ~m;
+                for (int q = 0; q < kBatch; ++q) {
+                    const int j = j0 + q * 64 + lane;
+                    uu[q] = j < w_hi ? pl[j] : 0u;
                 }
-                if (match && __ffsll((long long)peers) - 1 == lane)
-                    atomicAdd(&hist[bin], (unsigned)__popcll(peers));
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    const int j = j0 + q * 64 + lane;
+                    const bool f = j < w_hi && uu[q] >= t0;
+                    const unsigned long long bal = __ballot(f);
+                    if (f) {
+                        const int o = off + __popcll(bal & ((1ull << lane) - 1ull));
+                        cand_v[o] = uu[q];
+                        cand_j[o] = j;
+                    }
+                    off += __popcll(bal);
+                }
             }
+            __syncthreads();
+            unsigned remaining;
+            const unsigned thr = radix_select_block(
+                (unsigned)k, hist, sh, &s_digit, &s_remaining, remaining,
+                [&](unsigned prefix, unsigned mask, int shift, unsigned* h) {
+                    for (int i0 = 0; i0 < total; i0 += 1024) {       // uniform trip count
+                        const int i = i0 + tid;
+                        const unsigned u = i < total ? cand_v[i] : 0u;
+                        hist_add_wave(h, (u >> shift) & 255u, i < total && (u & mask) == prefix,
+                                      lane);
+                    }
+                });
+            // ordered output: thread t takes a contiguous run of the position-ordered candidates
+            const int chunk = (total + 1023) / 1024;
+            const int lo = min(total, tid * chunk), hi = min(total, lo + chunk);
+            int gt = 0, eq = 0;
+            for (int i = lo; i < hi; ++i) { gt += cand_v[i] > thr; eq += cand_v[i] == thr; }
+            int tot;
+            const int eq_before = block_scan_1024(eq, sh, tot);
+            int take = min(max((int)remaining - eq_before, 0), eq);
+            int pos = block_scan_1024(gt + take, sh, tot);
+            for (int i = lo; i < hi && pos < k; ++i) {
+                const unsigned u = cand_v[i];
+                if (u > thr) out[pos++] = cand_j[i];
+                else if (u == thr && take > 0) { out[pos++] = cand_j[i]; --take; }
+            }
+            return;
         }
-        __syncthreads();
-        // Find the bin where the count from the top first reaches `remaining`.
-        const int cnt = tid < 256 ? (int)hist[255 - tid] : 0;
-        int tot;
-        const int above = block_scan_1024(cnt, sh, tot);
-        if (tid < 256 && above < (int)remaining && above + cnt >= (int)remaining) {
-            s_digit = 255 - tid;
-            s_remaining = remaining - above;
-        }
-        __syncthreads();
-        prefix |= s_digit << shift;
-        mask |= 255u << shift;
-        remaining = s_remaining;
-        __syncthreads();
     }
-    const unsigned thr = prefix;     // k-th largest; `remaining` copies of it are kept
+
+    // Radix select of the k-th largest bit pattern over the whole pooled array (read from L2 on
+    // every pass), when the prefilter does not apply.
+    const int lane = tid & 63;
+    unsigned remaining;
+    const int n_pad = (n + 1023) / 1024 * 1024;
+    const unsigned thr = radix_select_block(
+        (unsigned)k, hist, sh, &s_digit, &s_remaining, remaining,
+        [&](unsigned prefix, unsigned mask, int shift, unsigned* h) {
+            for (int j0 = tid; j0 < n_pad; j0 += kBatch * 1024) {
+                unsigned uu[kBatch];
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    const int j = j0 + q * 1024;
+                    uu[q] = j < n ? pl[j] : 0u;
+                }
+#pragma unroll
+                for (int q = 0; q < kBatch; ++q) {
+                    const int j = j0 + q * 1024;
+                    if (j0 - tid + q * 1024 >= n_pad) break;      // uniform: whole 1024-blocks
+                    hist_add_wave(h, (uu[q] >> shift) & 255u, j < n && (uu[q] & mask) == prefix,
+                                  lane);
+                }
+            }
+        });
 
     const int chunk = (n + 1023) / 1024;
     const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);

@@ -84,3 +84,43 @@ def test_topk_budget_covering_the_context_is_decode():
                                     ns.block_table_np, L, 1 / math.sqrt(wl.head_dim))
     assert row_rel_err(host(out), ref) <= ATTN_RTOL
     assert lse_err(host(lse), ref_lse) <= 1e-4
+
+
+# Score patterns for the top-k over more than 32 * 1024 candidates (the kernel that pools from
+# global memory): key 0-th coordinates c_j from a few levels and every observation query along
+# the same axis make each position's score a function of c_j alone, so equal levels tie exactly.
+#   flat        every score equal: the k kept are the lowest positions
+#   rare_top    a rare top level covering more positions than the budget: ties at the threshold
+#   mid_ties    a rarer top level plus a level tied across thousands of positions
+#   big_budget  the generated (peaky) keys with a budget above 4096
+#   planted     the generated keys with a budget of 1024
+TIE_CASES = [("flat", (1.0,), (0.0,), 512), ("rare_top", (0.004, 0.1, 0.896), (3.0, 1.0, 0.0), 512),
+             ("mid_ties", (0.0005, 0.02, 0.9795), (3.0, 1.0, 0.0), 1024),
+             ("big_budget", None, None, 5000), ("planted", None, None, 1024)]
+
+
+@pytest.mark.parametrize("pattern,probs,levels,budget", TIE_CASES, ids=[c[0] for c in TIE_CASES])
+def test_long_context_topk_ties(pattern, probs, levels, budget):
+    torch.manual_seed(0)
+    wl = WORKLOADS["llama8b_ctx8k"]
+    ns = generate(wl, device="cuda", parts=("attn",), batch=2, prompt=(40000, 45000))
+    _, w, pool = wl.snapkv
+    print(f"\ntopk ties {pattern}: prompts {ns.prompt_lens_np.tolist()} budget {budget}", flush=True)
+    q_obs = ns.q_obs
+    if probs is not None:
+        rng = np.random.default_rng(7)
+        shape = ns.k_cache.shape[:3]
+        c = rng.choice(np.asarray(levels, dtype=np.float32), size=shape, p=probs)
+        ns.k_cache.zero_()
+        ns.k_cache[..., 0] = torch.from_numpy(c).to(ns.k_cache.dtype).cuda()
+        q_obs = torch.zeros_like(ns.q_obs)
+        q_obs[..., 0] = 8.0
+    kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.prompt_lens, ns.max_prompt)
+    sel, cnt, scores = kvss.snapkv_select(kv, q_obs, w, pool, budget, want_scores=True)
+    torch.cuda.synchronize()
+    g_c = host(scores).astype(np.float64)
+    o_sel, o_cnt = osnap.select_from_scores(g_c, ns.prompt_lens_np, w, pool, budget)
+    np.testing.assert_array_equal(host(cnt), o_cnt)
+    np.testing.assert_array_equal(host(sel), o_sel)
+    if pattern == "flat":
+        assert (host(sel) == np.arange(budget - w, dtype=np.int32)).all()
