@@ -120,7 +120,7 @@ int run_attention(kvss::AttnArgs& a, const Plan& p, bool gather, int dtype, void
 struct SnapLayout {
     Plan p1;
     int R, n_stride, xs_stride;
-    size_t part1, scores, pooled, xs, total;
+    size_t part1, rowc, scores, pooled, xs, total;
 };
 
 SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_scores) {
@@ -136,6 +136,7 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     s.n_stride = kv->max_kv_len > w ? kv->max_kv_len - w : 0;
     const size_t rows = (size_t)kv->batch * kv->num_kv_heads;
     s.part1 = align_up(rows * s.R * s.p1.nsplit * 2 * sizeof(float));
+    s.rowc = align_up(rows * s.R * sizeof(float));
     s.scores = own_scores ? align_up(rows * s.n_stride * sizeof(float)) : 0;
     s.pooled = align_up(rows * s.n_stride * sizeof(float));
     // With few rows the first pass keeps its scaled scores (4 R bytes per candidate, written
@@ -143,7 +144,7 @@ SnapLayout snap_layout(const kvss_kv* kv, int num_q_heads, int w, bool own_score
     const bool store = kv->dtype == KVSS_BF16 && s.R <= 16 && 4 * s.R < kv->head_dim;
     s.xs_stride = (s.n_stride + 3) / 4 * 4;
     s.xs = store ? align_up(rows * s.R * s.xs_stride * sizeof(float)) : 0;
-    s.total = s.part1 + s.scores + s.pooled + s.xs;
+    s.total = s.part1 + s.rowc + s.scores + s.pooled + s.xs;
     return s;
 }
 
@@ -374,11 +375,13 @@ int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads, int w, 
     a.nsplit1 = L.p1.nsplit;
     a.split_len1 = L.p1.split_len;
     a.part1 = reinterpret_cast<float*>(ws);
-    a.scores = scores_out ? scores_out : reinterpret_cast<float*>(ws + L.part1);
+    a.rowc = reinterpret_cast<float*>(ws + L.part1);
+    ws += L.part1 + L.rowc;
+    a.scores = scores_out ? scores_out : reinterpret_cast<float*>(ws);
     a.n_stride = L.n_stride;
-    a.pooled = reinterpret_cast<float*>(ws + L.part1 + L.scores);
+    a.pooled = reinterpret_cast<float*>(ws + L.scores);
     // (16-byte stores and loads; an unaligned workspace takes the path that re-reads K)
-    a.xs = L.xs > 0 && aligned16(ws) ? reinterpret_cast<float*>(ws + L.part1 + L.scores + L.pooled) : nullptr;
+    a.xs = L.xs > 0 && aligned16(ws) ? reinterpret_cast<float*>(ws + L.scores + L.pooled) : nullptr;
     a.xs_stride = L.xs_stride;
     a.pool = pool_kernel;
     a.keep = budget - w;

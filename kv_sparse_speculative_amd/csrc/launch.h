@@ -50,6 +50,7 @@ struct SnapArgs {
     float scale_log2;
     int nsplit1, split_len1;    // pass-1 key splits
     float* part1;               // [B*Hkv*R, nsplit1, 2] row (max, sum) partials, log2 domain
+    float* rowc;                // [B*Hkv*R] -(max + log2 sum) per row, merged from part1
     float* scores;              // [B, Hkv, n_stride] column scores
     int n_stride;               // max_kv_len - w
     float* pooled;              // [B, Hkv, n_stride] workspace

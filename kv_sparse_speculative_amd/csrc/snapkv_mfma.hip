@@ -15,7 +15,10 @@
 //   pass 2: S tile (16 rows x 16 keys) = Q . K^T, K as the B operand. Each lane holds 4 rows of
 //           one key column, so the column sum is an in-lane sum plus one cross-group reduction.
 // Scores use scale * log2(e) in float32 after the bf16 contraction; statistics are kept in the
-// log2 domain. Partials are written per split; pass 2 merges them per row in its prologue.
+// log2 domain. Partials are written per split; a small kernel between the passes merges them
+// into one constant per row, which every pass-2 workgroup of that (sequence, head) reads.
+// Each workgroup's prologue issues all of its small loads (block bases, queries, row constants)
+// before it waits for any, so it costs one memory round trip before the K stream starts.
 // A negative scale is folded into the staged queries (a bf16 sign flip is exact), so the
 // kernels only ever multiply by |scale| and the row maximum can be taken before scaling.
 // The hot loops are branch-free per lane: every 16-key tile lies in one cache block (splits and
@@ -39,46 +42,87 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const uint4& u) {
     return r;
 }
 
-// Q_obs rows of (b, g) -> LDS in MFMA operand order: entry (tile, ks, lane) holds
-// Q[row tile*16 + lane%16][ks*32 + (lane/16)*8 .. +7] (16 B); rows past R are zero.
-template <int D>
-__device__ void stage_queries(const SnapArgs& a, int b, int g, int NT, uint4* qs) {
+// Prologue staging, in one memory round trip: the block bases of keys [k0, k1) of (b, g) (TAB
+// entries at most), the observation queries of (b, g) in MFMA operand order and, when `rowc` is
+// given, the NT * 16 row constants of pass 2. All loads are issued before the first LDS write.
+// Query entry (tile, ks, lane) holds Q[row tile*16 + lane%16][ks*32 + (lane/16)*8 .. +7] (16 B);
+// rows past R are zero. Returns true if a block id of the range is invalid. The caller follows
+// with a barrier.
+template <int D, int NT, int TAB>
+__device__ bool stage_prologue(const SnapArgs& a, int b, int g, int k0, int k1, unsigned* tab,
+                               uint4* qs, const float* rowc, float* rowc_lds) {
     constexpr int KS = D / 32;
+    constexpr int NQ = NT * KS * 64;                     // query entries
+    constexpr int QPT = (NQ + kW * 64 - 1) / (kW * 64);
+    constexpr int TPT = (TAB + kW * 64 - 1) / (kW * 64);
+    constexpr int RPT = (NT * 16 + kW * 64 - 1) / (kW * 64);
+    const int tid = threadIdx.x;
+    const int blk0 = k1 > k0 ? k0 / a.bs : 0;
+    const int nblk = k1 > k0 ? (k1 - 1) / a.bs - blk0 + 1 : 0;
+    const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
+    int blk[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int e = tid + i * kW * 64;
+        blk[i] = e < nblk ? btab[blk0 + e] : 0;
+    }
     const uint16_t* qp = static_cast<const uint16_t*>(a.q_obs);
-    const unsigned flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-    for (int e = threadIdx.x; e < NT * KS * 64; e += kW * 64) {
+    uint4 qv[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int e = tid + i * kW * 64;
         const int lane = e & 63, ks = (e >> 6) % KS, t = (e >> 6) / KS;
         const int r = t * 16 + (lane & 15);
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < a.R) {
-            const int h = g * a.G + r / a.w, i = r % a.w;
-            v = *reinterpret_cast<const uint4*>(qp + (((size_t)b * a.Hq + h) * a.w + i) * D +
-                                                ks * 32 + (lane >> 4) * 8);
-            v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
+        qv[i] = make_uint4(0, 0, 0, 0);
+        if (e < NQ && r < a.R) {
+            const int h = g * a.G + r / a.w, qi = r % a.w;
+            qv[i] = *reinterpret_cast<const uint4*>(qp + (((size_t)b * a.Hq + h) * a.w + qi) * D +
+                                                    ks * 32 + (lane >> 4) * 8);
         }
-        qs[e] = v;
     }
-}
-
-// Block bases of the keys [k0, k1) of (b, g) -> LDS; returns false if a block id is invalid.
-__device__ bool stage_blocks(const SnapArgs& a, int b, int g, int k0, int k1, unsigned* tab) {
+    float rc[RPT];
+    if (rowc != nullptr) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = tid + i * kW * 64;
+            rc[i] = r < a.R ? rowc[((size_t)b * a.Hkv + g) * a.R + r] : kNegInf;
+        }
+    }
     bool bad = false;
-    if (k1 <= k0) return false;
-    const int blk0 = k0 / a.bs, nblk = (k1 - 1) / a.bs - blk0 + 1;
-    const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
-    for (int i = threadIdx.x; i < nblk; i += kW * 64) {
-        const int blk = btab[blk0 + i];
-        unsigned row = kBadRow;
-        if ((unsigned)blk < (unsigned)a.num_blocks) row = ((unsigned)blk * a.Hkv + g) * a.bs;
-        else bad = true;
-        tab[i] = row;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int e = tid + i * kW * 64;
+        if (e < nblk) {
+            unsigned row = kBadRow;
+            if ((unsigned)blk[i] < (unsigned)a.num_blocks) row = ((unsigned)blk[i] * a.Hkv + g) * a.bs;
+            else bad = true;
+            tab[e] = row;
+        }
+    }
+    const unsigned flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int e = tid + i * kW * 64;
+        uint4 v = qv[i];
+        v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
+        if (e < NQ) qs[e] = v;
+    }
+    if (rowc != nullptr) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = tid + i * kW * 64;
+            if (r < NT * 16) rowc_lds[r] = rc[i];
+        }
     }
     return bad;
 }
 
-// Load the K rows of one 32-key chunk (keys c0 .. c0+31, each 16 lanes x 16 B) into registers.
+// Load the K rows of one 32-key chunk (keys c0 .. c0+31, each 16 lanes x 16 B) into registers,
+// lane (m16, q4) of k-step ks holding row m16, dims ks*32 + q4*8 .. +7 (MFMA operand order).
 // c0 is wave-uniform and a multiple of 16, so each 16-key tile's block base is one uniform LDS
 // read. Keys outside [k0, k1) or with a bad block load row 0 and are reported as masked.
+// (Loading whole rows per instruction and reordering through LDS measured slower here: with the
+// score arithmetic in the loop the access pattern is not what limits these passes.)
 template <int D>
 __device__ __forceinline__ void load_k(const uint16_t* kp, const unsigned* tab, int bs, int sh,
                                        int blk0, int c0, int k1, int m16, int q4,
@@ -115,17 +159,40 @@ __device__ __forceinline__ void score_tile(const uint4 (&qv)[KS], const uint4 (&
 }
 
 // Row constant m + log2 l of observation row r of (b, g) from the pass-1 split partials (log2
-// domain): +inf for a row with no keys (it adds nothing), NaN if a split was poisoned.
-__device__ __forceinline__ float row_constant(const SnapArgs& a, int b, int g, int r) {
-    const float* pp = a.part1 + (((size_t)b * a.Hkv + g) * a.R + r) * a.nsplit1 * 2;
+// domain): +inf for a row with no keys (it adds nothing), NaN if a split was poisoned. Partials
+// are read eight at a time (two passes: the maximum, then the rescaled sum).
+__device__ float row_constant(const SnapArgs& a, int b, int g, int r) {
+    const float2* pp = reinterpret_cast<const float2*>(a.part1) +
+                       (((size_t)b * a.Hkv + g) * a.R + r) * a.nsplit1;
+    const int n = a.nsplit1;
+    constexpr int kU = 8;
     float M = kNegInf;
     bool nan = false;
-    for (int s = 0; s < a.nsplit1; ++s) { nan |= pp[2 * s] != pp[2 * s]; M = fmaxf(M, pp[2 * s]); }
+    for (int s0 = 0; s0 < n; s0 += kU) {
+        float m[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) m[u] = s0 + u < n ? pp[s0 + u].x : kNegInf;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) { nan |= m[u] != m[u]; M = fmaxf(M, m[u]); }
+    }
     float lam = 0.f;
     if (M != kNegInf)
-        for (int s = 0; s < a.nsplit1; ++s)
-            if (pp[2 * s] != kNegInf) lam += __builtin_amdgcn_exp2f(pp[2 * s] - M) * pp[2 * s + 1];
+        for (int s0 = 0; s0 < n; s0 += kU) {
+            float2 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) v[u] = s0 + u < n ? pp[s0 + u] : make_float2(kNegInf, 0.f);
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (v[u].x != kNegInf) lam += __builtin_amdgcn_exp2f(v[u].x - M) * v[u].y;
+        }
     return nan ? __builtin_nanf("") : (lam > 0.f ? M + __log2f(lam) : __builtin_huge_valf());
+}
+
+// Between the passes: -(row constant) of every observation row, once per (sequence, KV head).
+__global__ __launch_bounds__(256) void snap_rowconst_kernel(SnapArgs a) {
+    const int g = blockIdx.x, b = blockIdx.y;
+    for (int r = threadIdx.x; r < a.R; r += 256)
+        a.rowc[((size_t)b * a.Hkv + g) * a.R + r] = -row_constant(a, b, g, r);
 }
 
 template <int KS>
@@ -145,11 +212,11 @@ template <int D, int NT, bool STORE>
 __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(SnapArgs a) {
     static_assert(!STORE || NT == 1, "stored scores use one row tile");
     constexpr int KS = D / 32;
+
     constexpr int QS = NT * KS * 64 * 16;                  // queries in MFMA operand order
     constexpr int MS = 2 * kW * NT * 16 * 4;               // per-wave (max, sum), after the loop
     constexpr int TAB = (kSnapTableEntries + 1) * 4;
     __shared__ __attribute__((aligned(16))) unsigned char smem[(QS > MS ? QS : MS) + TAB];
-    __shared__ int s_bad;
     uint4* qs = reinterpret_cast<uint4*>(smem);
     float* sm = reinterpret_cast<float*>(smem);             // [kW][NT*16], reuses the queries
     float* sl = sm + kW * NT * 16;
@@ -166,13 +233,12 @@ __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(
     const int blk0 = div_bs(k0, bs, sh);
     // The planner keeps a split within one table; a longer one is refused (poisoned, not read).
     const bool fits = (k1 - k0) <= (kSnapTableEntries - 1) * bs;
-    if (tid == 0) s_bad = fits ? 0 : 1;
-    __syncthreads();
-    if (fits && stage_blocks(a, b, g, k0, k1, tab)) s_bad = 1;
     const int kend = fits ? k1 : k0;
-    __syncthreads();
+    const bool poisoned =
+        __syncthreads_or(!fits || stage_prologue<D, NT, kSnapTableEntries + 1>(
+                                      a, b, g, k0, kend, tab, qs, nullptr, nullptr)) != 0;
 
-    // The first two chunks are in flight while the queries are staged.
+    // The first two chunks are issued after the barrier (they need the block bases).
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     constexpr int stride = kW * 32;
     uint4 kA[2][KS], kB[2][KS];
@@ -180,8 +246,6 @@ __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(
     int c = k0 + wid * 32;
     load_k<D>(kp, tab, bs, sh, blk0, c, kend, m16, q4, kA, okA);
     load_k<D>(kp, tab, bs, sh, blk0, c + stride, kend, m16, q4, kB, okB);
-    stage_queries<D>(a, b, g, NT, qs);
-    __syncthreads();
 
     // Per lane: online (max, sum) of the scores it holds for row t*16 + m16; the maximum is
     // kept negated (nm = -m) so the exponent is one fma.
@@ -317,7 +381,6 @@ __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(
     for (int t = 0; t < NT; ++t)
         if (q4 == 0) { sm[wid * NT * 16 + t * 16 + m16] = -nm[t]; sl[wid * NT * 16 + t * 16 + m16] = lr[t]; }
     __syncthreads();
-    const bool poisoned = s_bad != 0;
     for (int r = tid; r < a.R; r += kW * 64) {
         float M = kNegInf;
 #pragma unroll
@@ -336,11 +399,11 @@ __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(
 template <int D, int NT>
 __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
     constexpr int KS = D / 32;
+
     constexpr int QS = NT * KS * 64 * 16;
     constexpr int TAB = (kSnapColKeys / 16 + 2) * 4;        // block bases of kSnapColKeys keys
     __shared__ __attribute__((aligned(16))) unsigned char smem[QS + TAB];
     __shared__ __attribute__((aligned(16))) float rowc[NT * 16];
-    __shared__ int s_bad;
     uint4* qs = reinterpret_cast<uint4*>(smem);
     unsigned* tab = reinterpret_cast<unsigned*>(smem + QS);
 
@@ -355,12 +418,13 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
     const int k1 = min(k0 + kSnapColKeys, n);
     const int bs = a.bs, sh = (bs & (bs - 1)) == 0 ? __builtin_ctz(bs) : -1;
     const int blk0 = div_bs(k0, bs, sh);
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-    if (stage_blocks(a, b, g, k0, k1, tab)) s_bad = 1;
-    __syncthreads();
+    // A operand of S = Q . K^T: lane supplies row m16 of the tile and dims q4*8.. of k-step ks,
+    // which is exactly the operand-order staging used for the B operand of pass 1. The row
+    // constants are negated (one fma per term).
+    const bool poisoned =
+        __syncthreads_or(stage_prologue<D, NT, kSnapColKeys / 16 + 2>(a, b, g, k0, k1, tab, qs,
+                                                                       a.rowc, rowc)) != 0;
 
-    // The first two chunks are in flight while the queries and row constants are staged.
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     constexpr int stride = kW * 32;
     uint4 kA[2][KS], kB[2][KS];
@@ -369,15 +433,7 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_mfma(SnapArgs a) {
     load_k<D>(kp, tab, bs, sh, blk0, c, k1, m16, q4, kA, okA);
     load_k<D>(kp, tab, bs, sh, blk0, c + stride, k1, m16, q4, kB, okB);
 
-    // A operand of S = Q . K^T: lane supplies row m16 of the tile and dims q4*8.. of k-step ks,
-    // which is exactly the operand-order staging used for the B operand of pass 1.
-    stage_queries<D>(a, b, g, NT, qs);
-    for (int r = tid; r < NT * 16; r += kW * 64)
-        rowc[r] = r < a.R ? -row_constant(a, b, g, r) : kNegInf;   // negated: one fma per term
-    __syncthreads();
-
     float* dst = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
-    const bool poisoned = s_bad != 0;
     const float sc = fabsf(a.scale_log2);
 
     auto consume = [&](int c0, const uint4 (&kr)[2][KS], const unsigned (&okm)[2]) {
@@ -436,7 +492,7 @@ __global__ __launch_bounds__(kW * 64) void snap_colscore_stored(SnapArgs a) {
     const int n = max(P - a.w, 0);
     const int k0 = tile * kStoredKeys;
     if (k0 >= n) return;
-    if (tid < a.R) rowc[tid] = -row_constant(a, b, g, tid);
+    if (tid < a.R) rowc[tid] = a.rowc[((size_t)b * a.Hkv + g) * a.R + tid];
     __syncthreads();
     const int j = k0 + 4 * tid;
     if (j >= n) return;
@@ -463,6 +519,8 @@ hipError_t launch_passes(const SnapArgs& a, hipStream_t s) {
             snap_rowstats_mfma<D, 1, true><<<dim3(a.nsplit1, a.Hkv, a.B), kW * 64, 0, s>>>(a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess || a.n_stride == 0) return e;
+            snap_rowconst_kernel<<<dim3(a.Hkv, a.B), 256, 0, s>>>(a);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
             const dim3 grid((a.n_stride + kStoredKeys - 1) / kStoredKeys, a.Hkv, a.B);
             snap_colscore_stored<<<grid, kW * 64, 0, s>>>(a);
             return hipGetLastError();
@@ -471,6 +529,8 @@ hipError_t launch_passes(const SnapArgs& a, hipStream_t s) {
     snap_rowstats_mfma<D, NT, false><<<dim3(a.nsplit1, a.Hkv, a.B), kW * 64, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_stride == 0) return e;
+    snap_rowconst_kernel<<<dim3(a.Hkv, a.B), 256, 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((a.n_stride + kSnapColKeys - 1) / kSnapColKeys, a.Hkv, a.B);
     snap_colscore_mfma<D, NT><<<grid, kW * 64, 0, s>>>(a);
     return hipGetLastError();
