@@ -218,6 +218,8 @@ KVSS_API int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads
  *     gives u'_x; a 32-bit word x maps to (x >> 9) * 2^-23 + 2^-24. Callers advance `offset`
  *     between calls that share a seed.
  *   Rows holding NaN or no finite logit give unspecified sampling draws (never an error).
+ *   The workspace holds the call's partials (no clearing needed); calls that overlap in time
+ *   need separate workspaces.
  *   Limits: 0 <= gamma <= 31 and batch <= 65535 (KVSS_EUNSUPPORTED above), 1 <= vocab < 2^24.
  *   out_tokens       int32 [batch, gamma + 1]: emitted tokens, then -1.
  *   out_num_accepted int32 [batch]: accepted draft tokens, 0 .. gamma.

@@ -393,7 +393,7 @@ int snapkv_select(const kvss_kv* kv, const void* q_obs, int num_q_heads, int w, 
 size_t kvss_accept_workspace_bytes(int batch, int gamma, int vocab) {
     if (batch < 0 || gamma < 0 || gamma > kMaxGamma || vocab <= 0) return 0;
     const kvss::AcceptPlan p = kvss::accept_plan(batch, gamma, vocab);
-    return align_up(p.parts_bytes + p.dec_bytes + p.race_bytes);
+    return align_up(p.parts_bytes + p.bonus_bytes + p.race_bytes + p.dec_bytes);
 }
 
 int spec_accept(const float* target_logits, const float* draft_logits, const int32_t* draft_tokens,

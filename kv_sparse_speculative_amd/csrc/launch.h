@@ -117,11 +117,11 @@ struct AcceptArgs {
     int32_t* out_num;           // [B]
 };
 
-// Workspace carve-up of one acceptance call: per-row slice partials, per-sequence decisions,
-// per-sequence race partials.
+// Workspace carve-up of one acceptance call: per-row slice partials, the statistics pass's race
+// keys over p_gamma, the race keys per slice, the decision per sequence.
 struct AcceptPlan {
     int nslice, nrace;
-    size_t parts_bytes, dec_bytes, race_bytes;
+    size_t parts_bytes, bonus_bytes, race_bytes, dec_bytes;
 };
 AcceptPlan accept_plan(int B, int gamma, int V);
 hipError_t launch_accept(const AcceptArgs& a, void* workspace, hipStream_t s);
