@@ -117,11 +117,11 @@ __device__ __forceinline__ int longest_first(const AttnArgs& a, int z, int lane)
 }
 
 // With one row tile the kernel fits two workgroups per CU (<= 256 registers per lane), so a
-// draft launch of B * Hkv workgroups is resident in a single round. FOLD (one row tile, R <= 8
-// query rows) puts the lo parts of P in tile rows R .. 2R - 1 instead of a second MFMA.
+// draft launch of B * Hkv workgroups is resident in a single round. FOLD (the last row tile
+// holds n <= 8 of the R query rows) puts the lo parts of that tile's P in its rows n .. 2n - 1
+// instead of a second MFMA: a draft's 4 rows, or a verify's rows 16 .. R - 1 for R <= 24.
 template <int D, bool GATHER, int NRT, bool FOLD>
 __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
-    static_assert(!FOLD || NRT == 1, "folded hi/lo rows need a single row tile");
     using C = MfmaCfg<D, NRT>;
     constexpr int NBUF = 2;            // chunks in flight per wave
     constexpr int KS = C::KS, DT = C::DT, STRIDE = C::STRIDE, ROWS = C::ROWS;
@@ -161,15 +161,17 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     }
 
     // Q^T as the B operand: lane supplies column (row) rt*16 + m16, dims ks*32 + q4*8 .. +7.
-    // Folded: columns R .. 2R - 1 repeat query rows 0 .. R - 1. (Issued with the prologue's
-    // other loads: the queries do not depend on the lengths.)
+    // Folded: in the last tile, with n = R - 16 (NRT - 1) rows, columns n .. 2n - 1 repeat
+    // that tile's rows 0 .. n - 1. (Issued with the prologue's other loads: the queries do
+    // not depend on the lengths.)
+    const int nlast = a.R - 16 * (NRT - 1);     // query rows in the last tile
     const uint16_t* qp = static_cast<const uint16_t*>(a.q);
     bf16x8 qop[NRT][KS];
     int qrow[NRT];                     // query row of this lane's column, or -1
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
         int r = rt * 16 + m16;
-        if (FOLD && r >= a.R && r < 2 * a.R) r -= a.R;
+        if (FOLD && rt == NRT - 1 && m16 >= nlast && m16 < 2 * nlast) r -= nlast;
         qrow[rt] = r < a.R ? r : -1;
         if (r < a.R) {
             const int h = g * a.G + r / a.T, t = r % a.T;
@@ -214,8 +216,8 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
         limit[rt] = (GATHER || qrow[rt] < 0) ? 0x7fffffff : L - a.T + qrow[rt] % a.T;
     // Every key below this position is visible to every query row (the first causal row).
     const int lim_all = GATHER ? 0x7fffffff : L - a.T;
-    // Folded: lanes of rows R .. 2R - 1 feed the lo parts of P to the PV product.
-    const bool lo_lane = FOLD && m16 >= a.R && m16 < 2 * a.R;
+    // Folded: lanes of the last tile's rows n .. 2n - 1 feed the lo parts of P to the PV product.
+    const bool lo_lane = FOLD && m16 >= nlast && m16 < 2 * nlast;
 
     f32x4 o[DT][NRT];
 #pragma unroll
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
                     const float p = __builtin_amdgcn_exp2f(sv[j] - muse);
                     const __bf16 hi = (__bf16)p;
                     const __bf16 lo_part = (__bf16)(p - (float)hi);
-                    if constexpr (FOLD) {
+                    if (FOLD && rt == NRT - 1) {
                         phi[rt][j] = lo_lane ? lo_part : hi;
                     } else {
                         phi[rt][j] = hi;
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt) {
                     o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi[rt], o[dt][rt], 0, 0, 0);
-                    if constexpr (!FOLD)
+                    if (!FOLD || rt < NRT - 1)
                         o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo[rt], o[dt][rt], 0, 0, 0);
                 }
             }
@@ -521,8 +523,8 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     __syncthreads();                 // every wave is done with its V tile (smem is reused)
     float* so = reinterpret_cast<float*>(smem);               // [wave][ROWS][D]
     float* sml = so + kWaves * ROWS * D;                       // [wave][ROWS][2]
-    // Rows that reach the output: R (and, folded, the lo rows R .. 2R - 1).
-    const int live = FOLD ? 2 * a.R : ROWS;
+    // Rows that reach the output: R (and, folded, the last tile's lo rows).
+    const int live = FOLD ? 16 * (NRT - 1) + 2 * nlast : ROWS;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
             for (int w = 0; w < kWaves; ++w) {
                 const float e = __builtin_amdgcn_exp2f(sml[(w * ROWS + r) * 2] - M);
                 float ow = so[(w * ROWS + r) * D + d];
-                if constexpr (FOLD) ow += so[(w * ROWS + r + a.R) * D + d];
+                if (FOLD && r >= 16 * (NRT - 1)) ow += so[(w * ROWS + r + nlast) * D + d];
                 lsum += e * sml[(w * ROWS + r) * 2 + 1];
                 osum += e * ow;
             }
@@ -590,15 +592,19 @@ void launch_d(const AttnArgs& a, bool gather, dim3 grid, dim3 block, hipStream_t
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool gather, hipStream_t s) {
     dim3 grid(a.nsplit, a.Hkv, a.B), block(kWaves * 64);
-    const bool one = a.R <= 16, fold = a.R <= 8;
+    // one row tile up to 16 rows, else two; the last tile is folded when it holds <= 8 rows
+    const bool one = a.R <= 16;
+    const bool fold = one ? a.R <= 8 : a.R <= 24;
     if (a.D == 128) {
-        if (fold) launch_d<128, 1, true>(a, gather, grid, block, s);
-        else if (one) launch_d<128, 1, false>(a, gather, grid, block, s);
-        else launch_d<128, 2, false>(a, gather, grid, block, s);
+        if (one) fold ? launch_d<128, 1, true>(a, gather, grid, block, s)
+                      : launch_d<128, 1, false>(a, gather, grid, block, s);
+        else fold ? launch_d<128, 2, true>(a, gather, grid, block, s)
+                  : launch_d<128, 2, false>(a, gather, grid, block, s);
     } else {
-        if (fold) launch_d<64, 1, true>(a, gather, grid, block, s);
-        else if (one) launch_d<64, 1, false>(a, gather, grid, block, s);
-        else launch_d<64, 2, false>(a, gather, grid, block, s);
+        if (one) fold ? launch_d<64, 1, true>(a, gather, grid, block, s)
+                      : launch_d<64, 1, false>(a, gather, grid, block, s);
+        else fold ? launch_d<64, 2, true>(a, gather, grid, block, s)
+                  : launch_d<64, 2, false>(a, gather, grid, block, s);
     }
     return hipGetLastError();
 }
