@@ -109,7 +109,8 @@ def rejection_accept(target, draft, tokens, temperature, seed, offset, seq_ids=N
     n_acc = np.zeros(B, dtype=np.int32)
     for b in range(B):
         p_rows = np.stack([softmax(target[b, i], temperature) for i in range(T)])
-        q_rows = np.stack([softmax(draft[b, i], temperature) for i in range(gamma)])
+        q_rows = (np.stack([softmax(draft[b, i], temperature) for i in range(gamma)])
+                  if gamma > 0 else np.zeros((0, V)))        # gamma = 0: only the draw from p_0
         sid = ids[b]
         emitted, n = rejection_accept_one(
             p_rows, q_rows, tokens[b],

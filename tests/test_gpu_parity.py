@@ -250,3 +250,25 @@ def test_verify_independent_of_split_plan():
     o1, _ = kvss.verify_attn_full(one, ns.q_verify[:1].contiguous())
     torch.cuda.synchronize()
     assert row_rel_err(host(o1), host(full[:1]).astype(np.float64)) <= 1e-5
+
+
+@pytest.mark.parametrize("gamma", [0, 1, 2])
+@pytest.mark.parametrize("vocab", [64, 9000])
+def test_accept_short_speculation_matches_oracle(gamma, vocab):
+    """Sampling acceptance at gamma 0-2: gamma = 0 emits only the draw from p_0, which the
+    statistics pass races for itself; with planted accepted prefixes and random drafts the
+    batch mixes that path with rejections at every position (one or several race slices)."""
+    wl = WORKLOADS["llama8b_ctx8k"]
+    ns = generate(wl, device="cuda", batch=24, parts=("accept",), vocab=vocab)
+    t = ns.target_logits[:, : gamma + 1].contiguous()
+    d = ns.draft_logits[:, :gamma].contiguous()
+    x = ns.draft_tokens[:, :gamma].contiguous()
+    seed, offset = 0xACCE97 + gamma, 5
+    for temp in (1.0, 0.6):
+        out, n_acc, _ = kvss.spec_accept(t, d, x, temp, seed, offset)
+        torch.cuda.synchronize()
+        r_out, r_n = oacc.spec_accept(host(t), host(d), host(x), temp, seed, offset)
+        np.testing.assert_array_equal(host(n_acc), r_n)
+        np.testing.assert_array_equal(host(out), r_out)
+        if gamma == 0:
+            assert (host(n_acc) == 0).all()

@@ -212,3 +212,18 @@ def test_greedy_accept_on_a_row_without_argmax():
     out, n = greedy_accept(t, np.array([[2, 1]], dtype=np.int32))
     assert n.tolist() == [1] and out.tolist() == [[2, -1, -1]]
     assert draft_sample(np.array([[np.nan, np.nan], [-np.inf, -np.inf]]), 0.0).tolist() == [-1, 0]
+
+
+def test_rejection_accept_without_drafts_is_one_draw_from_p0():
+    """gamma = 0 (Section 3.1 with no speculation): nothing to accept, one token emitted by the
+    exponential race over p_0 with the race uniforms of position 0."""
+    rng = np.random.default_rng(11)
+    B, V = 3, 50
+    target = rng.normal(size=(B, 1, V)) * 2.0
+    draft = np.zeros((B, 0, V))
+    tokens = np.zeros((B, 0), dtype=np.int32)
+    out, n = rejection_accept(target, draft, tokens, 0.8, seed=9, offset=2)
+    assert (n == 0).all() and out.shape == (B, 1)
+    for b in range(B):
+        p = softmax(target[b, 0], 0.8)
+        assert out[b, 0] == exponential_race(p, race_uniforms(9, 2, b, 0, V))
