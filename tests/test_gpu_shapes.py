@@ -1,7 +1,8 @@
 """GPU parity on shapes outside the five measured workloads, so that every compiled kernel
 variant runs against the oracle: bf16 with head_dim 64, block sizes 32 and 64, a single query
 head per KV head (G = 1, the stored-score SnapKV pass) and eight (G = 8, the largest verify
-tile of 32 query rows), SnapKV row-tile counts 1, 4 and 6, and the fp32 path at head_dim 128.
+tile of 32 query rows), SnapKV row-tile counts 1, 4 and 6, the fp32 path at head_dim 128, and
+verify row counts 17, 20 (head_dim 64) and 24 (the last 16-row tile folded) and 25 (not).
 
 Each workload is ragged or shuffled and spans several blocks, splits and a partial last block.
 """
@@ -36,6 +37,16 @@ SHAPES = [
              block_size=32, seed=2004),
     Workload("f32_d128_g5", "f32", 2, 10, 2, 128, (300, 500), 2, (4, 60), (72, 8, 7), 1000,
              seed=2005),
+    # verify row counts at the folded-last-tile boundaries: 17 and 24 rows (head_dim 128), 20
+    # rows at head_dim 64, and 25 rows (two tiles, not folded)
+    Workload("bf16_r17_g1", "bf16", 2, 4, 4, 128, (400, 700), 16, (4, 28), (64, 8, 5), 1000,
+             block_size=16, shuffled_blocks=True, seed=2006),
+    Workload("bf16_r24_g8", "bf16", 2, 16, 2, 128, (500, 900), 2, (8, 56), (96, 8, 7), 1000,
+             block_size=32, seed=2007),
+    Workload("bf16_d64_r20_g4", "bf16", 3, 16, 4, 64, (300, 1000), 4, (4, 60), (80, 16, 7), 1000,
+             block_size=16, shuffled_blocks=True, seed=2008),
+    Workload("bf16_r25_g5", "bf16", 2, 10, 2, 128, (600, 800), 4, (4, 28), (64, 8, 3), 1000,
+             block_size=64, seed=2009),
 ]
 IDS = [w.name for w in SHAPES]
 
