@@ -420,27 +420,115 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     }
 }
 
-// Register-resident pool + top-k for up to 1024 * MAXC candidates (MAXC 16 or 32), same
+// Register-resident pool + top-k for up to 1024 * MAXC candidates (MAXC 8, 16 or 32), same
 // selection rule as snap_topk_kernel (centred max-pool, k largest by IEEE bits, ties to the
-// lower position, ascending output):
-//   1. the scores of one (sequence, KV head) are read once, coalesced, into LDS (one pad word
-//      per 32 so that reading a thread's contiguous run is conflict-free);
-//   2. thread t takes the contiguous positions [t*C, t*C + C) plus the pool halo from LDS and
-//      keeps the pooled values in registers;
-//   3. four MSB-first radix passes count digits into per-wave LDS histograms (no cross-wave
-//      contention; each thread adds runs of equal digits once) and pick the digit of the k-th
-//      largest with one block scan;
-//   4. an ordered compaction writes the kept positions.
+// lower position, ascending output). The kernel is bound by vector instructions per position
+// (16 waves share a CU's 4 SIMDs), so every step is kept branch-free and short:
+//   1. the scores of one (sequence, KV head) are read once, coalesced, into LDS: position p at
+//      word 4 + p + p / MAXC (a pad word after every MAXC, so a thread's run starts at an odd
+//      multiple and reading runs is conflict-free; 4 words in front for the first halo);
+//   2. thread t owns positions [t*MAXC, t*MAXC + MAXC); it reads them and a halo of kPoolHalo
+//      on each side at static offsets from one address (NaN reads as -inf; only the first wave
+//      and the waves reaching the end of the range mask by position) and pools them with
+//      three-input maxima: every triple, then one more maximum per position;
+//   3. prefilter: the positions fall into groups (each thread's run split by position mod 2,
+//      else mod 4 or mod 8, the coarsest of these splits that gives at least k non-empty groups).
+//      The top 16 bits of the k-th largest group maximum form a bound t0 that at least k pooled
+//      values reach, so every kept value is >= t0. The values >= t0 are compacted into LDS in
+//      position order and four radix passes over them alone find the k-th largest. A pass is
+//      one barrier: the shared 256-bin histogram is filled (one LDS atomic per wave when all
+//      its matching lanes share a digit), then every wave picks the digit itself with a DPP
+//      scan; histograms rotate over three buffers, so clearing the next one needs no barrier;
+//   4. an ordered compaction of the candidates writes the kept positions.
+//   Where no split gives k groups, or the values >= t0 do not fit in LDS, steps 3 and 4 run
+//   over all pooled values in registers instead (per-wave histograms fed by runs of equal
+//   digits, the digit picked with a block scan).
 constexpr int kPoolHalo = 3;   // register path: pool kernels up to 2 * kPoolHalo + 1
 constexpr int kTopkWaves = 16;
 constexpr size_t kTopkMaxLds = 150 * 1024;  // dynamic LDS of the register path (of 160 KB)
 
+// Words of dynamic LDS of the register path: the padded scores of 1024 runs plus the halos.
+__host__ __device__ constexpr size_t topk_reg_words(int maxc) { return 1024 * (size_t)(maxc + 1) + 8; }
+
+// Inclusive prefix sum over the 64 lanes of a wave (GFX9 DPP: row shifts, then row broadcasts).
+__device__ __forceinline__ unsigned wave_scan_incl(unsigned x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);    // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);    // row_bcast:31
+    return x;
+}
+
+// Exclusive prefix sum over the 1024 threads of a workgroup with one barrier: every thread adds
+// up the wave totals below it itself. `sh` must not be written again until every thread has
+// returned.
+__device__ __forceinline__ unsigned block_scan_1024_flat(unsigned v, unsigned* sh, unsigned& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const unsigned x = wave_scan_incl(v);
+    if (lane == 63) sh[wid] = x;
+    __syncthreads();
+    unsigned before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const unsigned s = sh[w];
+        tot += s;
+        before += w < wid ? s : 0u;
+    }
+    total = tot;
+    return before + x - v;
+}
+
+// Adds one to bin `bin` of `hist` for every lane with `match`: a single atomic for the wave
+// when all matching lanes share the bin (a head's scores share their high digits), one per
+// lane otherwise. Every lane of the wave must call it.
+__device__ __forceinline__ void hist_add_lanes(unsigned* hist, unsigned bin, bool match, int lane) {
+    const unsigned long long act = __ballot(match);
+    if (act == 0ull) return;
+    const int first = __builtin_ctzll(act);
+    const unsigned b0 = __builtin_amdgcn_readlane(bin, first);
+    if (__ballot(match && bin != b0) == 0ull) {
+        if (lane == first) atomicAdd(&hist[b0], (unsigned)__popcll(act));
+    } else if (match) {
+        atomicAdd(&hist[bin], 1u);
+    }
+}
+
+// Every lane of a wave, after the 256-bin histogram (16-byte aligned) is complete: the bin,
+// counting from the top, where the running count first reaches `remaining` (which the total
+// reaches), and the count still needed inside that bin. Lane l reads bins 252 - 4l .. 255 - 4l.
+__device__ __forceinline__ void pick_digit(const unsigned* hist, unsigned remaining, int lane,
+                                           unsigned& digit, unsigned& rem_out) {
+    const uint4 hv = reinterpret_cast<const uint4*>(hist)[63 - lane];
+    const unsigned s = hv.x + hv.y + hv.z + hv.w;
+    const unsigned incl = wave_scan_incl(s);
+    unsigned acc = incl - s;
+    const int at = __builtin_ctzll(__ballot(acc < remaining && incl >= remaining));
+    unsigned bin = 255u - 4u * lane;
+    if (acc + hv.w < remaining) {
+        acc += hv.w; --bin;
+        if (acc + hv.z < remaining) {
+            acc += hv.z; --bin;
+            if (acc + hv.y < remaining) { acc += hv.y; --bin; }
+        }
+    }
+    digit = __builtin_amdgcn_readlane(bin, at);
+    rem_out = remaining - __builtin_amdgcn_readlane(acc, at);
+}
+
+// Runs of 8 or 16 leave room for two workgroups per CU (37 or 70 KB of LDS) when a wave holds at
+// most 64 registers, i.e. eight waves per SIMD.
 template <int MAXC>
-__global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
-    extern __shared__ float lds_scores[];            // n + n/32 floats, then histograms
+__global__ __launch_bounds__(1024, MAXC <= 16 ? 8 : 4) void snap_topk_reg_kernel(SnapArgs a) {
+    static_assert(MAXC == 8 || MAXC == 16 || MAXC == 32, "run length");
+    constexpr int LOG2C = MAXC == 8 ? 3 : MAXC == 16 ? 4 : 5;
+    extern __shared__ float lds_scores[];            // padded scores, then candidates or histograms
+    __shared__ __attribute__((aligned(16))) unsigned hist[3][256];
+    __shared__ unsigned shu[16];
     __shared__ int sh[16];
     __shared__ unsigned s_digit, s_remaining;
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wid = tid >> 6;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
     const int n = max(P - a.w, 0);
     const int k = a.keep;
@@ -451,42 +539,157 @@ __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
         return;
     }
     const float* c = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
+    if (tid < 64) reinterpret_cast<uint4*>(hist[0])[tid] = make_uint4(0u, 0u, 0u, 0u);
     {
-        // all of a thread's loads are issued before any is waited on (n <= 1024 * MAXC)
+        // all of a thread's loads are issued before any is waited on; indices past n re-read
+        // the last score (stored beyond the range, never used unmasked)
         float tmp[MAXC];
 #pragma clang loop unroll(full)
-        for (int q = 0; q < MAXC; ++q) {
-            const int j = tid + q * 1024;
-            tmp[q] = j < n ? c[j] : 0.f;
-        }
+        for (int q = 0; q < MAXC; ++q) tmp[q] = c[min(tid + q * 1024, n - 1)];
+        float* dst = lds_scores + 4 + tid + (tid >> LOG2C);
 #pragma clang loop unroll(full)
-        for (int q = 0; q < MAXC; ++q) {
-            const int j = tid + q * 1024;
-            if (j < n) lds_scores[j + (j >> 5)] = tmp[q];
-        }
+        for (int q = 0; q < MAXC; ++q) dst[q * (1024 + (1024 >> LOG2C))] = tmp[q];
     }
     __syncthreads();
 
-    const int C = (n + 1023) / 1024;
-    const int base = tid * C;
+    const int base = tid * MAXC;
+    const int lc = min(max(n - base, 0), MAXC);      // live positions of this thread
     const int r = a.pool / 2;
+    // win[q] holds position base - kPoolHalo + q; the pooled value of base + e goes to win[e]
     float win[MAXC + 2 * kPoolHalo];
+    {
+        const float* src = lds_scores + tid * (MAXC + 1);      // position base - 4 + i at src[i]
+        auto word = [](int q) { return q < kPoolHalo ? q : q < MAXC + kPoolHalo ? q + 1 : q + 2; };
+        // interior waves: every position of the runs and halos lies in [0, n)
+        const bool inner = wid > 0 && (64 * wid + 64) * MAXC + kPoolHalo <= n;
+        if (inner) {
 #pragma clang loop unroll(full)
-    for (int q = 0; q < MAXC + 2 * kPoolHalo; ++q) {
-        const int p = base - kPoolHalo + q;
-        const bool use = q >= kPoolHalo - r && q < kPoolHalo + C + r && p >= 0 && p < n;
-        win[q] = use ? lds_scores[p + (p >> 5)] : kNegInf;
+            for (int q = 0; q < MAXC + 2 * kPoolHalo; ++q) win[q] = fmaxf(src[word(q)], kNegInf);
+        } else {
+#pragma clang loop unroll(full)
+            for (int q = 0; q < MAXC + 2 * kPoolHalo; ++q) {
+                const int p = base - kPoolHalo + q;
+                win[q] = (p >= 0 && p < n) ? fmaxf(src[word(q)], kNegInf) : kNegInf;
+            }
+        }
     }
-    // pooled value of position base + e overwrites win[e] (no later position reads it)
+    {
+        float r1[MAXC + 2 * kPoolHalo - 2];           // r1[i]: maximum of win[i .. i + 2]
 #pragma clang loop unroll(full)
-    for (int e = 0; e < MAXC; ++e) {
-        float m = kNegInf;
+        for (int i = 0; i < MAXC + 2 * kPoolHalo - 2; ++i)
+            r1[i] = fmaxf(fmaxf(win[i], win[i + 1]), win[i + 2]);
+        if (r == 0) {
 #pragma clang loop unroll(full)
-        for (int d = -kPoolHalo; d <= kPoolHalo; ++d)
-            if (d >= -r && d <= r) m = fmaxf(m, win[e + kPoolHalo + d]);
-        win[e] = m;
+            for (int e = 0; e < MAXC; ++e) win[e] = win[e + 3];
+        } else if (r == 1) {
+#pragma clang loop unroll(full)
+            for (int e = 0; e < MAXC; ++e) win[e] = r1[e + 2];
+        } else if (r == 2) {
+#pragma clang loop unroll(full)
+            for (int e = 0; e < MAXC; ++e) win[e] = fmaxf(r1[e + 1], r1[e + 3]);
+        } else {
+#pragma clang loop unroll(full)
+            for (int e = 0; e < MAXC; ++e) win[e] = fmaxf(fmaxf(r1[e], r1[e + 2]), r1[e + 4]);
+        }
     }
-    auto live = [&](int e) { return e < C && base + e < n; };
+    auto live = [&](int e) { return e < lc; };
+
+    // Group maxima by position mod 8 within the run; coarser groups merge them.
+    unsigned gm[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma clang loop unroll(full)
+    for (int e = 0; e < MAXC; ++e)
+        gm[e & 7] = max(gm[e & 7], live(e) ? __float_as_uint(win[e]) : 0u);
+    const int tfull = n >> LOG2C, rem = n - (tfull << LOG2C);   // full runs, then the rest
+    auto ngroups = [&](int S) { return tfull * S + min(S, rem); };
+    // Finer groups give a tighter bound (a pooled maximum repeats over the pool window, so the
+    // groups mod 2 already split most repeats) at more values to rank; mod 2 measured best.
+    const int S = ngroups(2) >= k ? 2 : ngroups(4) >= k ? 4 : ngroups(8) >= k ? 8 : 0;
+    if (S > 0) {
+        // group s < S: the positions e of the run with e mod S == s
+        unsigned g4[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) g4[s] = max(gm[s], gm[s + 4]);
+        const unsigned g2[2] = {max(g4[0], g4[2]), max(g4[1], g4[3])};
+        unsigned gs[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) gs[s] = S == 8 ? gm[s] : S == 4 ? g4[s & 3] : g2[s & 1];
+        int hb = 0;                                   // histogram buffer of the current pass
+        // one radix pass over the offered values: histogram, one barrier, digit in every wave
+        auto pass_end = [&](unsigned& prefix, unsigned& mask, unsigned& remaining, int shift) {
+            if (tid < 64) reinterpret_cast<uint4*>(hist[hb == 2 ? 0 : hb + 1])[tid] = make_uint4(0u, 0u, 0u, 0u);
+            __syncthreads();
+            unsigned d, rr;
+            pick_digit(hist[hb], remaining, lane, d, rr);
+            prefix |= d << shift;
+            mask |= 255u << shift;
+            remaining = rr;
+            hb = hb == 2 ? 0 : hb + 1;
+        };
+        // t0: the top 16 bits of the k-th largest maximum over the non-empty groups
+        unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = 24 - 8 * pass;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                if (s < S)
+                    hist_add_lanes(hist[hb], (gs[s] >> shift) & 255u,
+                                   s < lc && (gs[s] & mask) == prefix, lane);
+            pass_end(prefix, mask, remaining, shift);
+        }
+        const unsigned t0 = prefix;
+        unsigned cm = 0;                              // this thread's candidates, bit e
+#pragma clang loop unroll(full)
+        for (int e = 0; e < MAXC; ++e)
+            cm |= (live(e) && __float_as_uint(win[e]) >= t0 ? 1u : 0u) << e;
+        unsigned nc;
+        unsigned off = block_scan_1024_flat(__popc(cm), shu, nc);
+        if (nc <= topk_reg_words(MAXC) / 2) {
+            // Every wave is past its pooling reads (the barriers above), so the staged scores
+            // can be overwritten: (bit pattern, position) pairs in position order.
+            uint2* cand = reinterpret_cast<uint2*>(lds_scores);
+#pragma clang loop unroll(full)
+            for (int e = 0; e < MAXC; ++e)
+                if ((cm >> e) & 1u) cand[off++] = make_uint2(__float_as_uint(win[e]), (unsigned)(base + e));
+            __syncthreads();
+            prefix = 0;
+            mask = 0;
+            remaining = (unsigned)k;
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+                for (unsigned i0 = 0; i0 < nc; i0 += 1024) {   // uniform trip count
+                    const unsigned i = i0 + tid;
+                    const unsigned u = i < nc ? cand[i].x : 0u;
+                    hist_add_lanes(hist[hb], (u >> shift) & 255u, i < nc && (u & mask) == prefix,
+                                   lane);
+                }
+                pass_end(prefix, mask, remaining, shift);
+            }
+            const unsigned thr = prefix;
+            // ordered output: thread t takes a contiguous run of the candidates; one scan
+            // counts, below each thread, the values above thr (low half) and equal to it (high)
+            const unsigned chunk = (nc + 1023) / 1024;
+            const unsigned lo = min(nc, tid * chunk), hi = min(nc, lo + chunk);
+            unsigned gt = 0, eq = 0;
+            for (unsigned i = lo; i < hi; ++i) {
+                const unsigned u = cand[i].x;
+                gt += u > thr;
+                eq += u == thr;
+            }
+            unsigned tot;
+            const unsigned below = block_scan_1024_flat(gt | (eq << 16), shu, tot);  // nc < 2^16
+            // values equal to thr taken below this thread (the lowest positions go first)
+            const unsigned eq_taken = min(below >> 16, remaining);
+            unsigned take = min(remaining - eq_taken, eq);
+            unsigned pos = (below & 0xffffu) + eq_taken;
+            for (unsigned i = lo; i < hi && pos < (unsigned)k; ++i) {
+                const uint2 cv = cand[i];
+                if (cv.x > thr) out[pos++] = (int)cv.y;
+                else if (cv.x == thr && take > 0) { out[pos++] = (int)cv.y; --take; }
+            }
+            return;
+        }
+    }
+
     __syncthreads();                                  // the score staging area is reused below
     unsigned* whist = reinterpret_cast<unsigned*>(lds_scores);      // [kTopkWaves][256]
 
@@ -551,33 +754,25 @@ __global__ __launch_bounds__(1024) void snap_topk_reg_kernel(SnapArgs a) {
     }
 }
 
-// LDS of the register path: padded scores (>= the per-wave histograms).
-size_t topk_reg_smem(int n_stride) {
-    const size_t scores = (size_t)(n_stride + n_stride / 32 + 1) * 4;
-    const size_t hist = (size_t)kTopkWaves * 256 * 4;
-    return scores > hist ? scores : hist;
+template <int MAXC>
+hipError_t launch_topk_reg(const SnapArgs& a, dim3 grid, hipStream_t s) {
+    const size_t smem = topk_reg_words(MAXC) * 4;
+    static_assert(topk_reg_words(32) * 4 <= kTopkMaxLds, "LDS");
+    // dynamic LDS beyond the default 64 KB must be allowed per kernel
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&snap_topk_reg_kernel<MAXC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    snap_topk_reg_kernel<MAXC><<<grid, 1024, smem, s>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const SnapArgs& a, hipStream_t s) {
     const dim3 grid(a.Hkv, a.B);
     const int C = (a.n_stride + 1023) / 1024;
-    const size_t smem = topk_reg_smem(a.n_stride);
-    if (a.pool / 2 <= kPoolHalo && smem <= kTopkMaxLds) {
-        // dynamic LDS beyond the default 64 KB must be allowed per kernel
-        if (C <= 16) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&snap_topk_reg_kernel<16>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (e != hipSuccess) return e;
-            snap_topk_reg_kernel<16><<<grid, 1024, smem, s>>>(a);
-            return hipGetLastError();
-        }
-        if (C <= 32) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&snap_topk_reg_kernel<32>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (e != hipSuccess) return e;
-            snap_topk_reg_kernel<32><<<grid, 1024, smem, s>>>(a);
-            return hipGetLastError();
-        }
+    if (a.pool / 2 <= kPoolHalo) {
+        if (C <= 8) return launch_topk_reg<8>(a, grid, s);
+        if (C <= 16) return launch_topk_reg<16>(a, grid, s);
+        if (C <= 32) return launch_topk_reg<32>(a, grid, s);
     }
     snap_topk_kernel<<<grid, 1024, 0, s>>>(a);
     return hipGetLastError();

@@ -86,26 +86,38 @@ def test_topk_budget_covering_the_context_is_decode():
     assert lse_err(host(lse), ref_lse) <= 1e-4
 
 
-# Score patterns for the top-k over more than 32 * 1024 candidates (the kernel that pools from
-# global memory): key 0-th coordinates c_j from a few levels and every observation query along
-# the same axis make each position's score a function of c_j alone, so equal levels tie exactly.
-#   flat        every score equal: the k kept are the lowest positions
+# Score patterns for both top-k kernels: the one that pools from global memory (more than
+# 32 * 1024 candidates, prompts of 40k-45k) and the register-resident one (prompts of 20k-30k).
+# Key 0-th coordinates c_j from a few levels and every observation query along the same axis make
+# each position's score a function of c_j alone, so equal levels tie exactly.
+#   flat        every score equal: the k kept are the lowest positions (the register kernel's
+#               prefilter keeps every position, more than fit in LDS: its all-register path)
 #   rare_top    a rare top level covering more positions than the budget: ties at the threshold
 #   mid_ties    a rarer top level plus a level tied across thousands of positions
-#   big_budget  the generated (peaky) keys with a budget above 4096
-#   planted     the generated keys with a budget of 1024
+#   planted     the generated (peaky) keys with a budget of 1024 (register kernel: groups by
+#               position mod 2 within each 32-position run; ties of a pooled maximum split
+#               across the budget)
+#   planted_2   budget 1500 (register kernel: mod 2, barely enough groups at the shorter prompt)
+#   planted_4   budget 2500 (register kernel: groups by position mod 4)
+#   big_budget  budget 5000 (register kernel: groups by position mod 8)
+#   huge_budget budget 6000 (register kernel: fewer than k groups even mod 8, so no prefilter)
 TIE_CASES = [("flat", (1.0,), (0.0,), 512), ("rare_top", (0.004, 0.1, 0.896), (3.0, 1.0, 0.0), 512),
              ("mid_ties", (0.0005, 0.02, 0.9795), (3.0, 1.0, 0.0), 1024),
-             ("big_budget", None, None, 5000), ("planted", None, None, 1024)]
+             ("planted", None, None, 1024), ("planted_2", None, None, 1500),
+             ("planted_4", None, None, 2500), ("big_budget", None, None, 5000),
+             ("huge_budget", None, None, 6000)]
+REGIMES = [("global", (40000, 45000)), ("register", (20000, 30000))]
 
 
+@pytest.mark.parametrize("regime,prompt", REGIMES, ids=[r[0] for r in REGIMES])
 @pytest.mark.parametrize("pattern,probs,levels,budget", TIE_CASES, ids=[c[0] for c in TIE_CASES])
-def test_long_context_topk_ties(pattern, probs, levels, budget):
+def test_long_context_topk_ties(pattern, probs, levels, budget, regime, prompt):
     torch.manual_seed(0)
     wl = WORKLOADS["llama8b_ctx8k"]
-    ns = generate(wl, device="cuda", parts=("attn",), batch=2, prompt=(40000, 45000))
+    ns = generate(wl, device="cuda", parts=("attn",), batch=2, prompt=prompt)
     _, w, pool = wl.snapkv
-    print(f"\ntopk ties {pattern}: prompts {ns.prompt_lens_np.tolist()} budget {budget}", flush=True)
+    print(f"\ntopk ties {pattern} ({regime}): prompts {ns.prompt_lens_np.tolist()} budget {budget}",
+          flush=True)
     q_obs = ns.q_obs
     if probs is not None:
         rng = np.random.default_rng(7)
