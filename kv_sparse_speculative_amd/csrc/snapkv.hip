@@ -13,6 +13,8 @@
 // The score passes run on the vector ALU with the queries staged in LDS; they are
 // bit-deterministic (fixed key order per thread, no atomics on floats).
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -221,19 +223,119 @@ __device__ unsigned radix_select_block(unsigned k, unsigned* hist, int* sh, unsi
     return prefix;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (GFX9 DPP: row shifts, then row broadcasts).
+__device__ __forceinline__ unsigned wave_scan_incl(unsigned x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);    // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);    // row_bcast:31
+    return x;
+}
+
+// Exclusive prefix sum over the 1024 threads of a workgroup with one barrier: every thread adds
+// up the wave totals below it itself. `sh` must not be written again until every thread has
+// returned.
+__device__ __forceinline__ unsigned block_scan_1024_flat(unsigned v, unsigned* sh, unsigned& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const unsigned x = wave_scan_incl(v);
+    if (lane == 63) sh[wid] = x;
+    __syncthreads();
+    unsigned before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const unsigned s = sh[w];
+        tot += s;
+        before += w < wid ? s : 0u;
+    }
+    total = tot;
+    return before + x - v;
+}
+
+// Adds one to bin `bin` of `hist` for every lane with `match`: a single atomic for the wave
+// when all matching lanes share the bin (a head's scores share their high digits), one per
+// lane otherwise. Every lane of the wave must call it.
+__device__ __forceinline__ void hist_add_lanes(unsigned* hist, unsigned bin, bool match, int lane) {
+    const unsigned long long act = __ballot(match);
+    if (act == 0ull) return;
+    const int first = __builtin_ctzll(act);
+    const unsigned b0 = __builtin_amdgcn_readlane(bin, first);
+    if (__ballot(match && bin != b0) == 0ull) {
+        if (lane == first) atomicAdd(&hist[b0], (unsigned)__popcll(act));
+    } else if (match) {
+        atomicAdd(&hist[bin], 1u);
+    }
+}
+
+// Every lane of a wave, after the 256-bin histogram (16-byte aligned) is complete: the bin,
+// counting from the top, where the running count first reaches `remaining` (which the total
+// reaches), and the count still needed inside that bin. Lane l reads bins 252 - 4l .. 255 - 4l.
+__device__ __forceinline__ void pick_digit(const unsigned* hist, unsigned remaining, int lane,
+                                           unsigned& digit, unsigned& rem_out) {
+    const uint4 hv = reinterpret_cast<const uint4*>(hist)[63 - lane];
+    const unsigned s = hv.x + hv.y + hv.z + hv.w;
+    const unsigned incl = wave_scan_incl(s);
+    unsigned acc = incl - s;
+    const int at = __builtin_ctzll(__ballot(acc < remaining && incl >= remaining));
+    unsigned bin = 255u - 4u * lane;
+    if (acc + hv.w < remaining) {
+        acc += hv.w; --bin;
+        if (acc + hv.z < remaining) {
+            acc += hv.z; --bin;
+            if (acc + hv.y < remaining) { acc += hv.y; --bin; }
+        }
+    }
+    digit = __builtin_amdgcn_readlane(bin, at);
+    rem_out = remaining - __builtin_amdgcn_readlane(acc, at);
+}
+
+// End of one radix pass in the one-barrier scheme (every thread of the workgroup calls it): the
+// caller has added this pass's digits to hist[hb]; the next buffer is cleared (three rotate, so
+// the one cleared was last read two passes ago), the workgroup waits once, and every wave picks
+// the digit from hist[hb] itself.
+__device__ __forceinline__ void radix_pass_end(unsigned (*hist)[256], int& hb, unsigned& prefix,
+                                               unsigned& mask, unsigned& remaining, int shift) {
+    const int tid = threadIdx.x;
+    const int next = hb == 2 ? 0 : hb + 1;
+    if (tid < 64) reinterpret_cast<uint4*>(hist[next])[tid] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    unsigned d, rr;
+    pick_digit(hist[hb], remaining, tid & 63, d, rr);
+    prefix |= d << shift;
+    mask |= 255u << shift;
+    remaining = rr;
+    hb = next;
+}
+
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format); with stride 0 and num_records
+// in bytes, an access at or past num_records is dropped (stores) or reads 0 (loads).
+constexpr int kBufferWord3 = 0x00020000;
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations (lgkmcnt 0) but
+// not for its global loads in flight (which __syncthreads() would drain), then joins the barrier.
+// It orders nothing in global memory; the compiler still waits for each load before its use.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0); vmcnt and expcnt left as they are
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Prefilter of the generic top-k: candidates held in LDS (bit pattern and position), and the
 // number of position groups whose maxima bound the selection from below.
 constexpr int kPreCap = 7680;      // 60 KB: the static LDS stays within the default 64 KB
 constexpr int kPreGroups = 8192;
 
 __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
-    __shared__ unsigned hist[256];
+    __shared__ __attribute__((aligned(16))) unsigned hist[3][256];
     __shared__ int sh[16];
+    __shared__ unsigned shu[16];
     __shared__ unsigned s_digit, s_remaining;
-    __shared__ unsigned cand_v[kPreCap];
+    __shared__ __attribute__((aligned(16))) unsigned cand_v[kPreCap];
     __shared__ int cand_j[kPreCap];
     __shared__ int wcnt[16];
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int P = max(min(a.prompt_lens[b], a.max_kv_len), 0);
     const int n = max(P - a.w, 0);
     const int k = a.keep;
@@ -246,67 +348,164 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
     const float* c = a.scores + ((size_t)b * a.Hkv + g) * a.n_stride;
     unsigned* pl = reinterpret_cast<unsigned*>(a.pooled + ((size_t)b * a.Hkv + g) * a.n_stride);
     const int r = a.pool / 2;
+    if (tid < 64) reinterpret_cast<uint4*>(hist[0])[tid] = make_uint4(0u, 0u, 0u, 0u);
     // Every loop below issues a batch of independent loads before using any (the pooled array
     // is re-read from L2 on every pass; one load at a time would wait out its latency each).
     constexpr int kBatch = 8;
-    static_assert(kBatch * 1024 == kPreGroups, "group j mod kPreGroups is slot q of thread j % 1024");
+    static_assert(kBatch * 1024 == kPreGroups, "each thread holds kBatch of the j mod kPreGroups groups");
     unsigned gmax[kBatch];       // maximum pooled bit pattern of this thread's groups
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) gmax[q] = 0u;
-    for (int j0 = tid; j0 < n; j0 += kBatch * 1024) {
-        float m[kBatch];
+    // Pooling. A neighbour out of [0, n) is -inf; the centre is the score itself.
+    constexpr int kTile = 4096, kTileLoads = (kTile + 8 + 1023) / 1024;
+    static_assert(kTileLoads * 1024 <= kPreCap, "every staged word lies in the candidate area");
+    if (r <= 3) {
+        // Tiles of 4096 positions staged through LDS (the candidate area, not yet in use): word
+        // i holds position j0 - 4 + i. Thread t pools positions j0 + 4t .. j0 + 4t + 3 from the
+        // 12 words 4t .. 4t + 11 (three 16-byte reads) with three-input maxima.
+        // Every load of the loop is unconditional, so the compiler counts them and waits for
+        // each tile's loads only where they are used. A whole tile's pooled values go out as one
+        // 16-byte store per lane (when the row is 16-byte aligned); the tile holding position n - 1 uses buffer stores that the
+        // hardware drops past n. The loads of the next kAhead tiles are in flight while one is
+        // pooled; the last round may pool up to three tiles past the end, whose stores are all
+        // dropped.
+        constexpr int kAhead = 4;
+        float* tile = reinterpret_cast<float*>(cand_v);
+        const int ntiles = (n + kTile - 1) / kTile;
+        const __amdgpu_buffer_rsrc_t plr =
+            __builtin_amdgcn_make_buffer_rsrc(pl, (short)0, n * 4, kBufferWord3);
+        const bool pl16 = (reinterpret_cast<uintptr_t>(pl) & 15) == 0;
+        // scores through a buffer resource: positions outside [0, n) read as 0 without an access
+        // (a negative position wraps to a huge offset) and are set to -inf in LDS
+        const __amdgpu_buffer_rsrc_t cr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(c), (short)0, n * 4, kBufferWord3);
+        float v[kAhead][kTileLoads];
+        auto load_tile = [&](int t, float (&dst)[kTileLoads]) {
+            const int j0 = t * kTile;
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int j = j0 + q * 1024;
-            m[q] = j < n ? c[j] : 0.f;
+            for (int q = 0; q < kTileLoads; ++q)
+                dst[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       cr, (j0 - 4 + tid + 1024 * q) * 4, 0, 0));
+        };
+        // group slot of position j0 + 4t + e: 4 (t mod 2) + e, i.e. group j mod kPreGroups
+        auto pool_tile = [&](int t, float (&buf)[kTileLoads], auto half) {
+            constexpr int H = decltype(half)::value;
+            const int j0 = t * kTile;
+            lds_barrier();                            // the previous tile's reads are done
+#pragma unroll
+            for (int q = 0; q < kTileLoads; ++q) tile[tid + 1024 * q] = buf[q];
+            if (j0 < 4 || j0 + kTile + 4 > n) {      // the tile reaches past either end
+#pragma unroll
+                for (int q = 0; q < kTileLoads; ++q) {
+                    const int p = j0 - 4 + tid + 1024 * q;
+                    if (p < 0 || p >= n) tile[tid + 1024 * q] = kNegInf;
+                }
+            }
+            lds_barrier();
+            load_tile(t + kAhead, buf);
+            const float4 w0 = reinterpret_cast<const float4*>(tile)[tid];
+            const float4 w1 = reinterpret_cast<const float4*>(tile)[tid + 1];
+            const float4 w2 = reinterpret_cast<const float4*>(tile)[tid + 2];
+            const float w[12] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y, w2.z, w2.w};
+            // position j0 + 4t + e is w[4 + e]; its window is w[4 + e - r .. 4 + e + r]
+            float pm[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float m = w[4 + e];
+                if (r >= 1) m = fmaxf(m, fmaxf(w[3 + e], w[5 + e]));
+                if (r >= 2) m = fmaxf(m, fmaxf(w[2 + e], w[6 + e]));
+                if (r >= 3) m = fmaxf(m, fmaxf(w[1 + e], w[7 + e]));
+                pm[e] = m;
+            }
+            if (j0 + kTile <= n && pl16) {           // a whole tile: one 16-byte store per lane
+                *reinterpret_cast<uint4*>(pl + j0 + 4 * tid) =
+                    make_uint4(__float_as_uint(pm[0]), __float_as_uint(pm[1]),
+                               __float_as_uint(pm[2]), __float_as_uint(pm[3]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pm[e]), plr,
+                                                          (j0 + 4 * tid + e) * 4, 0, 0);
+            }
+            if (j0 + kTile <= n) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gmax[4 * H + e] = max(gmax[4 * H + e], __float_as_uint(pm[e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gmax[4 * H + e] = max(gmax[4 * H + e], j0 + 4 * tid + e < n ? __float_as_uint(pm[e]) : 0u);
+            }
+        };
+        static_assert(kAhead == 4, "tile t uses buffer t mod 4 and slot half t mod 2");
+#pragma unroll
+        for (int t = 0; t < kAhead; ++t) load_tile(t, v[t]);
+        for (int t = 0; t < ntiles; t += kAhead) {
+            pool_tile(t, v[0], std::integral_constant<int, 0>{});
+            pool_tile(t + 1, v[1], std::integral_constant<int, 1>{});
+            pool_tile(t + 2, v[2], std::integral_constant<int, 0>{});
+            pool_tile(t + 3, v[3], std::integral_constant<int, 1>{});
         }
-        for (int d = 1; d <= r; ++d) {
+    } else {
+        for (int j0 = tid; j0 < n; j0 += kBatch * 1024) {
+            float m[kBatch];
 #pragma unroll
             for (int q = 0; q < kBatch; ++q) {
                 const int j = j0 + q * 1024;
-                const float lft = (j < n && j - d >= 0) ? c[j - d] : kNegInf;
-                const float rgt = (j + d < n) ? c[j + d] : kNegInf;
-                m[q] = fmaxf(m[q], fmaxf(lft, rgt));
+                m[q] = j < n ? c[j] : 0.f;
             }
-        }
+            for (int d = 1; d <= r; ++d) {
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int j = j0 + q * 1024;
-            if (j < n) {
-                pl[j] = __float_as_uint(m[q]);
-                gmax[q] = max(gmax[q], __float_as_uint(m[q]));
+                for (int q = 0; q < kBatch; ++q) {
+                    const int j = j0 + q * 1024;
+                    const float lft = (j < n && j - d >= 0) ? c[j - d] : kNegInf;
+                    const float rgt = (j + d < n) ? c[j + d] : kNegInf;
+                    m[q] = fmaxf(m[q], fmaxf(lft, rgt));
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int j = j0 + q * 1024;
+                if (j < n) {
+                    pl[j] = __float_as_uint(m[q]);
+                    gmax[q] = max(gmax[q], __float_as_uint(m[q]));
+                }
             }
         }
     }
     __syncthreads();
 
-    // Prefilter. The positions fall into kPreGroups groups (j mod kPreGroups); the k-th largest
-    // group maximum t0 is reached by at least k pooled values, so every value kept is >= t0.
-    // When the values >= t0 fit in LDS they are compacted there in position order and the
-    // selection runs over them alone; otherwise it runs over the whole pooled array below.
+    // Prefilter. The positions fall into kPreGroups groups (j mod kPreGroups); the top 16 bits
+    // of the k-th largest group maximum form a bound t0 that at least k pooled values reach, so
+    // every value kept is >= t0. When the values >= t0 fit in LDS they are compacted there in
+    // position order and the selection runs over them alone; otherwise it runs over the whole
+    // pooled array below. Radix passes take one barrier each (radix_pass_end).
     if (k <= kPreGroups / 2) {
-        const int lane = tid & 63, wid = tid >> 6;
-        unsigned rem0;
-        const unsigned t0 = radix_select_block(
-            (unsigned)k, hist, sh, &s_digit, &s_remaining, rem0,
-            [&](unsigned prefix, unsigned mask, int shift, unsigned* h) {
+        int hb = 0;
+        unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = 24 - 8 * pass;
 #pragma unroll
-                for (int q = 0; q < kBatch; ++q)
-                    hist_add_wave(h, (gmax[q] >> shift) & 255u, (gmax[q] & mask) == prefix, lane);
-            });
+            for (int q = 0; q < kBatch; ++q)
+                hist_add_lanes(hist[hb], (gmax[q] >> shift) & 255u, (gmax[q] & mask) == prefix, lane);
+            radix_pass_end(hist, hb, prefix, mask, remaining, shift);
+        }
+        const unsigned t0 = prefix;
         // each wave takes one contiguous span of positions (a multiple of 64): count, then place
+        // (16 loads in flight per lane: the pooled array comes back from L2 or the last-level cache)
+        constexpr int kScan = 16;
         const int span = (n + 16 * 64 - 1) / (16 * 64) * 64;
         const int w_lo = min(n, wid * span), w_hi = min(n, w_lo + span);
         int cnt = 0;
-        for (int j0 = w_lo; j0 < w_hi; j0 += kBatch * 64) {
-            unsigned uu[kBatch];
+        for (int j0 = w_lo; j0 < w_hi; j0 += kScan * 64) {
+            unsigned uu[kScan];
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
+            for (int q = 0; q < kScan; ++q) {
                 const int j = j0 + q * 64 + lane;
-                uu[q] = j < w_hi ? pl[j] : 0u;
+                const unsigned x = pl[min(j, w_hi - 1)];          // unconditional: no branch
+                uu[q] = j < w_hi ? x : 0u;
             }
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q)
+            for (int q = 0; q < kScan; ++q)
                 cnt += __popcll(__ballot(j0 + q * 64 + lane < w_hi && uu[q] >= t0));
         }
         if (lane == 0) wcnt[wid] = cnt;
@@ -317,15 +516,16 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
             total += wcnt[w2];
         }
         if (total <= kPreCap) {
-            for (int j0 = w_lo; j0 < w_hi; j0 += kBatch * 64) {
-                unsigned uu[kBatch];
+            for (int j0 = w_lo; j0 < w_hi; j0 += kScan * 64) {
+                unsigned uu[kScan];
 #pragma unroll
-                for (int q = 0; q < kBatch; ++q) {
+                for (int q = 0; q < kScan; ++q) {
                     const int j = j0 + q * 64 + lane;
-                    uu[q] = j < w_hi ? pl[j] : 0u;
+                    const unsigned x = pl[min(j, w_hi - 1)];          // unconditional: no branch
+                    uu[q] = j < w_hi ? x : 0u;
                 }
 #pragma unroll
-                for (int q = 0; q < kBatch; ++q) {
+                for (int q = 0; q < kScan; ++q) {
                     const int j = j0 + q * 64 + lane;
                     const bool f = j < w_hi && uu[q] >= t0;
                     const unsigned long long bal = __ballot(f);
@@ -338,27 +538,34 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
                 }
             }
             __syncthreads();
-            unsigned remaining;
-            const unsigned thr = radix_select_block(
-                (unsigned)k, hist, sh, &s_digit, &s_remaining, remaining,
-                [&](unsigned prefix, unsigned mask, int shift, unsigned* h) {
-                    for (int i0 = 0; i0 < total; i0 += 1024) {       // uniform trip count
-                        const int i = i0 + tid;
-                        const unsigned u = i < total ? cand_v[i] : 0u;
-                        hist_add_wave(h, (u >> shift) & 255u, i < total && (u & mask) == prefix,
-                                      lane);
-                    }
-                });
-            // ordered output: thread t takes a contiguous run of the position-ordered candidates
+            prefix = 0;
+            mask = 0;
+            remaining = (unsigned)k;
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+                for (int i0 = 0; i0 < total; i0 += 1024) {       // uniform trip count
+                    const int i = i0 + tid;
+                    const unsigned u = i < total ? cand_v[i] : 0u;
+                    hist_add_lanes(hist[hb], (u >> shift) & 255u, i < total && (u & mask) == prefix,
+                                   lane);
+                }
+                radix_pass_end(hist, hb, prefix, mask, remaining, shift);
+            }
+            const unsigned thr = prefix;
+            // ordered output: thread t takes a contiguous run of the position-ordered
+            // candidates; one scan counts, below each thread, the values above thr (low half)
+            // and equal to it (high half; total < 2^16)
             const int chunk = (total + 1023) / 1024;
             const int lo = min(total, tid * chunk), hi = min(total, lo + chunk);
-            int gt = 0, eq = 0;
+            unsigned gt = 0, eq = 0;
             for (int i = lo; i < hi; ++i) { gt += cand_v[i] > thr; eq += cand_v[i] == thr; }
-            int tot;
-            const int eq_before = block_scan_1024(eq, sh, tot);
-            int take = min(max((int)remaining - eq_before, 0), eq);
-            int pos = block_scan_1024(gt + take, sh, tot);
-            for (int i = lo; i < hi && pos < k; ++i) {
+            unsigned tot;
+            const unsigned below = block_scan_1024_flat(gt | (eq << 16), shu, tot);
+            // values equal to thr taken below this thread (the lowest positions go first)
+            const unsigned eq_taken = min(below >> 16, remaining);
+            unsigned take = min(remaining - eq_taken, eq);
+            unsigned pos = (below & 0xffffu) + eq_taken;
+            for (int i = lo; i < hi && pos < (unsigned)k; ++i) {
                 const unsigned u = cand_v[i];
                 if (u > thr) out[pos++] = cand_j[i];
                 else if (u == thr && take > 0) { out[pos++] = cand_j[i]; --take; }
@@ -369,11 +576,10 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
 
     // Radix select of the k-th largest bit pattern over the whole pooled array (read from L2 on
     // every pass), when the prefilter does not apply.
-    const int lane = tid & 63;
     unsigned remaining;
     const int n_pad = (n + 1023) / 1024 * 1024;
     const unsigned thr = radix_select_block(
-        (unsigned)k, hist, sh, &s_digit, &s_remaining, remaining,
+        (unsigned)k, hist[0], sh, &s_digit, &s_remaining, remaining,
         [&](unsigned prefix, unsigned mask, int shift, unsigned* h) {
             for (int j0 = tid; j0 < n_pad; j0 += kBatch * 1024) {
                 unsigned uu[kBatch];
@@ -449,73 +655,6 @@ constexpr size_t kTopkMaxLds = 150 * 1024;  // dynamic LDS of the register path 
 
 // Words of dynamic LDS of the register path: the padded scores of 1024 runs plus the halos.
 __host__ __device__ constexpr size_t topk_reg_words(int maxc) { return 1024 * (size_t)(maxc + 1) + 8; }
-
-// Inclusive prefix sum over the 64 lanes of a wave (GFX9 DPP: row shifts, then row broadcasts).
-__device__ __forceinline__ unsigned wave_scan_incl(unsigned x) {
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);    // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);    // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);    // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);    // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);    // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);    // row_bcast:31
-    return x;
-}
-
-// Exclusive prefix sum over the 1024 threads of a workgroup with one barrier: every thread adds
-// up the wave totals below it itself. `sh` must not be written again until every thread has
-// returned.
-__device__ __forceinline__ unsigned block_scan_1024_flat(unsigned v, unsigned* sh, unsigned& total) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const unsigned x = wave_scan_incl(v);
-    if (lane == 63) sh[wid] = x;
-    __syncthreads();
-    unsigned before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        const unsigned s = sh[w];
-        tot += s;
-        before += w < wid ? s : 0u;
-    }
-    total = tot;
-    return before + x - v;
-}
-
-// Adds one to bin `bin` of `hist` for every lane with `match`: a single atomic for the wave
-// when all matching lanes share the bin (a head's scores share their high digits), one per
-// lane otherwise. Every lane of the wave must call it.
-__device__ __forceinline__ void hist_add_lanes(unsigned* hist, unsigned bin, bool match, int lane) {
-    const unsigned long long act = __ballot(match);
-    if (act == 0ull) return;
-    const int first = __builtin_ctzll(act);
-    const unsigned b0 = __builtin_amdgcn_readlane(bin, first);
-    if (__ballot(match && bin != b0) == 0ull) {
-        if (lane == first) atomicAdd(&hist[b0], (unsigned)__popcll(act));
-    } else if (match) {
-        atomicAdd(&hist[bin], 1u);
-    }
-}
-
-// Every lane of a wave, after the 256-bin histogram (16-byte aligned) is complete: the bin,
-// counting from the top, where the running count first reaches `remaining` (which the total
-// reaches), and the count still needed inside that bin. Lane l reads bins 252 - 4l .. 255 - 4l.
-__device__ __forceinline__ void pick_digit(const unsigned* hist, unsigned remaining, int lane,
-                                           unsigned& digit, unsigned& rem_out) {
-    const uint4 hv = reinterpret_cast<const uint4*>(hist)[63 - lane];
-    const unsigned s = hv.x + hv.y + hv.z + hv.w;
-    const unsigned incl = wave_scan_incl(s);
-    unsigned acc = incl - s;
-    const int at = __builtin_ctzll(__ballot(acc < remaining && incl >= remaining));
-    unsigned bin = 255u - 4u * lane;
-    if (acc + hv.w < remaining) {
-        acc += hv.w; --bin;
-        if (acc + hv.z < remaining) {
-            acc += hv.z; --bin;
-            if (acc + hv.y < remaining) { acc += hv.y; --bin; }
-        }
-    }
-    digit = __builtin_amdgcn_readlane(bin, at);
-    rem_out = remaining - __builtin_amdgcn_readlane(acc, at);
-}
 
 // Runs of 8 or 16 leave room for two workgroups per CU (37 or 70 KB of LDS) when a wave holds at
 // most 64 registers, i.e. eight waves per SIMD.
@@ -614,17 +753,6 @@ __global__ __launch_bounds__(1024, MAXC <= 16 ? 8 : 4) void snap_topk_reg_kernel
 #pragma unroll
         for (int s = 0; s < 8; ++s) gs[s] = S == 8 ? gm[s] : S == 4 ? g4[s & 3] : g2[s & 1];
         int hb = 0;                                   // histogram buffer of the current pass
-        // one radix pass over the offered values: histogram, one barrier, digit in every wave
-        auto pass_end = [&](unsigned& prefix, unsigned& mask, unsigned& remaining, int shift) {
-            if (tid < 64) reinterpret_cast<uint4*>(hist[hb == 2 ? 0 : hb + 1])[tid] = make_uint4(0u, 0u, 0u, 0u);
-            __syncthreads();
-            unsigned d, rr;
-            pick_digit(hist[hb], remaining, lane, d, rr);
-            prefix |= d << shift;
-            mask |= 255u << shift;
-            remaining = rr;
-            hb = hb == 2 ? 0 : hb + 1;
-        };
         // t0: the top 16 bits of the k-th largest maximum over the non-empty groups
         unsigned prefix = 0, mask = 0, remaining = (unsigned)k;
         for (int pass = 0; pass < 2; ++pass) {
@@ -634,7 +762,7 @@ __global__ __launch_bounds__(1024, MAXC <= 16 ? 8 : 4) void snap_topk_reg_kernel
                 if (s < S)
                     hist_add_lanes(hist[hb], (gs[s] >> shift) & 255u,
                                    s < lc && (gs[s] & mask) == prefix, lane);
-            pass_end(prefix, mask, remaining, shift);
+            radix_pass_end(hist, hb, prefix, mask, remaining, shift);
         }
         const unsigned t0 = prefix;
         unsigned cm = 0;                              // this thread's candidates, bit e
@@ -662,7 +790,7 @@ __global__ __launch_bounds__(1024, MAXC <= 16 ? 8 : 4) void snap_topk_reg_kernel
                     hist_add_lanes(hist[hb], (u >> shift) & 255u, i < nc && (u & mask) == prefix,
                                    lane);
                 }
-                pass_end(prefix, mask, remaining, shift);
+                radix_pass_end(hist, hb, prefix, mask, remaining, shift);
             }
             const unsigned thr = prefix;
             // ordered output: thread t takes a contiguous run of the candidates; one scan
