@@ -116,6 +116,82 @@ __device__ __forceinline__ int longest_first(const AttnArgs& a, int z, int lane)
     return hit != 0ull ? __builtin_amdgcn_readlane(found, __ffsll((long long)hit) - 1) : z;
 }
 
+// Cross-wave merge of one workgroup's results: every wave left its (max, sum) per row in sml
+// ([wave][ROWS][2]) and its O rows in so ([wave][ROWS][D]); with one split the normalised
+// output (and LSE) is written, otherwise the (m, l, o) partial of `split`. Each thread merges 4
+// consecutive dims of one row per step: the waves' (m, l) of the row as four 8-byte reads,
+// their outputs as 16-byte reads, the result as 16-byte (output) or 8-byte (split partial)
+// stores.
+template <int D, int NRT, bool FOLD>
+__device__ __forceinline__ void merge_out(const AttnArgs& a, const float* so, const float* sml,
+                                          int nlast, int b, int g, int split, bool poisoned,
+                                          int tid) {
+    constexpr int ROWS = 16 * NRT;
+    const float qnan = __builtin_nanf("");
+    constexpr int D4 = D / 4;
+    const float2* sml2 = reinterpret_cast<const float2*>(sml);  // (m, l) of [wave][row]
+    const bool out16 = (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
+    const bool part8 = (reinterpret_cast<uintptr_t>(a.part) & 7) == 0;
+    for (int idx = tid; idx < a.R * D4; idx += kWaves * 64) {
+        const int r = idx / D4, d = (idx % D4) * 4;
+        float2 ml[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) ml[w] = sml2[w * ROWS + r];
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w].x);
+        float lsum = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float e = __builtin_amdgcn_exp2f(ml[w].x - M);
+                float4 ow = *reinterpret_cast<const float4*>(so + (w * ROWS + r) * D + d);
+                if (FOLD && r >= 16 * (NRT - 1)) {
+                    const float4 lo = *reinterpret_cast<const float4*>(so + (w * ROWS + r + nlast) * D + d);
+                    ow.x += lo.x; ow.y += lo.y; ow.z += lo.z; ow.w += lo.w;
+                }
+                lsum += e * ml[w].y;
+                o0 += e * ow.x;
+                o1 += e * ow.y;
+                o2 += e * ow.z;
+                o3 += e * ow.w;
+            }
+        }
+        const int h = g * a.G + r / a.T, t = r % a.T;
+        const size_t row = ((size_t)b * a.Hq + h) * a.T + t;
+        if (a.nsplit == 1) {
+            float4 ov = lsum > 0.f ? make_float4(o0 / lsum, o1 / lsum, o2 / lsum, o3 / lsum)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            if (poisoned) ov = make_float4(qnan, qnan, qnan, qnan);
+            float* dst = a.out + row * D + d;
+            if (out16) {
+                *reinterpret_cast<float4*>(dst) = ov;
+            } else {
+                dst[0] = ov.x; dst[1] = ov.y; dst[2] = ov.z; dst[3] = ov.w;
+            }
+            if (d == 0 && a.lse != nullptr) {
+                float lv = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : kNegInf;
+                a.lse[row] = poisoned ? qnan : lv;
+            }
+        } else {
+            // a partial is D + 2 floats: 8-byte aligned when the workspace is
+            float* pp = a.part + (row * a.nsplit + split) * (D + 2);
+            const float2 p01 = poisoned ? make_float2(qnan, qnan) : make_float2(o0, o1);
+            const float2 p23 = poisoned ? make_float2(qnan, qnan) : make_float2(o2, o3);
+            if (part8) {
+                *reinterpret_cast<float2*>(pp + d) = p01;
+                *reinterpret_cast<float2*>(pp + d + 2) = p23;
+            } else {
+                pp[d] = p01.x; pp[d + 1] = p01.y; pp[d + 2] = p23.x; pp[d + 3] = p23.y;
+            }
+            if (d == 0) {
+                pp[D] = poisoned ? qnan : M;
+                pp[D + 1] = poisoned ? qnan : lsum;
+            }
+        }
+    }
+}
+
 // With one row tile the kernel fits two workgroups per CU (<= 256 registers per lane), so a
 // draft launch of B * Hkv workgroups is resident in a single round. FOLD (the last row tile
 // holds n <= 8 of the R query rows) puts the lo parts of that tile's P in its rows n .. 2n - 1
@@ -543,73 +619,7 @@ __global__ __launch_bounds__(kWaves * 64, NRT == 1 ? 2 : 1) void attn_mfma_kerne
     }
     __syncthreads();
 
-    const bool poisoned = s_bad != 0;
-    const float qnan = __builtin_nanf("");
-    // Each thread merges 4 consecutive dims of one row per step: the waves' (m, l) of the row
-    // as four 8-byte reads, their outputs as 16-byte reads, the result as 16-byte (output) or
-    // 8-byte (split partial) stores.
-    constexpr int D4 = D / 4;
-    const float2* sml2 = reinterpret_cast<const float2*>(sml);  // (m, l) of [wave][row]
-    const bool out16 = (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
-    const bool part8 = (reinterpret_cast<uintptr_t>(a.part) & 7) == 0;
-    for (int idx = tid; idx < a.R * D4; idx += kWaves * 64) {
-        const int r = idx / D4, d = (idx % D4) * 4;
-        float2 ml[kWaves];
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) ml[w] = sml2[w * ROWS + r];
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w].x);
-        float lsum = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-        if (M != kNegInf) {
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float e = __builtin_amdgcn_exp2f(ml[w].x - M);
-                float4 ow = *reinterpret_cast<const float4*>(so + (w * ROWS + r) * D + d);
-                if (FOLD && r >= 16 * (NRT - 1)) {
-                    const float4 lo = *reinterpret_cast<const float4*>(so + (w * ROWS + r + nlast) * D + d);
-                    ow.x += lo.x; ow.y += lo.y; ow.z += lo.z; ow.w += lo.w;
-                }
-                lsum += e * ml[w].y;
-                o0 += e * ow.x;
-                o1 += e * ow.y;
-                o2 += e * ow.z;
-                o3 += e * ow.w;
-            }
-        }
-        const int h = g * a.G + r / a.T, t = r % a.T;
-        const size_t row = ((size_t)b * a.Hq + h) * a.T + t;
-        if (a.nsplit == 1) {
-            float4 ov = lsum > 0.f ? make_float4(o0 / lsum, o1 / lsum, o2 / lsum, o3 / lsum)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-            if (poisoned) ov = make_float4(qnan, qnan, qnan, qnan);
-            float* dst = a.out + row * D + d;
-            if (out16) {
-                *reinterpret_cast<float4*>(dst) = ov;
-            } else {
-                dst[0] = ov.x; dst[1] = ov.y; dst[2] = ov.z; dst[3] = ov.w;
-            }
-            if (d == 0 && a.lse != nullptr) {
-                float lv = lsum > 0.f ? (M + __log2f(lsum)) * kLn2 : kNegInf;
-                a.lse[row] = poisoned ? qnan : lv;
-            }
-        } else {
-            // a partial is D + 2 floats: 8-byte aligned when the workspace is
-            float* pp = a.part + (row * a.nsplit + split) * (D + 2);
-            const float2 p01 = poisoned ? make_float2(qnan, qnan) : make_float2(o0, o1);
-            const float2 p23 = poisoned ? make_float2(qnan, qnan) : make_float2(o2, o3);
-            if (part8) {
-                *reinterpret_cast<float2*>(pp + d) = p01;
-                *reinterpret_cast<float2*>(pp + d + 2) = p23;
-            } else {
-                pp[d] = p01.x; pp[d + 1] = p01.y; pp[d + 2] = p23.x; pp[d + 3] = p23.y;
-            }
-            if (d == 0) {
-                pp[D] = poisoned ? qnan : M;
-                pp[D + 1] = poisoned ? qnan : lsum;
-            }
-        }
-    }
+    merge_out<D, NRT, FOLD>(a, so, sml, nlast, b, g, split, s_bad != 0, tid);
 }
 
 template <int D, int NRT, bool FOLD>
