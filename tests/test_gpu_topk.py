@@ -136,3 +136,26 @@ def test_long_context_topk_ties(pattern, probs, levels, budget, regime, prompt):
     np.testing.assert_array_equal(host(sel), o_sel)
     if pattern == "flat":
         assert (host(sel) == np.arange(budget - w, dtype=np.int32)).all()
+
+
+# Pool kernels 1 to 9 on both top-k kernels. Over more than 32k candidates (45001-token
+# prompts) the global-memory kernel pools through LDS tiles for radii up to 3 and reads its
+# neighbours from global memory above; the odd row stride of its pooled workspace leaves most
+# (sequence, head) rows not 16-byte aligned (the tile stores then take the range-checked path).
+# At 25001 tokens the register kernel takes radii up to 3 and the global-memory kernel radius 4.
+@pytest.mark.parametrize("prompt", [45001, 25001])
+@pytest.mark.parametrize("pool", [1, 3, 5, 7, 9])
+def test_long_context_pool_sizes(pool, prompt):
+    torch.manual_seed(0)
+    wl = WORKLOADS["llama8b_ctx8k"]
+    ns = generate(wl, device="cuda", parts=("attn",), batch=2, prompt=(prompt, prompt))
+    _, w, _ = wl.snapkv
+    budget = 1024
+    kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.prompt_lens, ns.max_prompt)
+    sel, cnt, scores = kvss.snapkv_select(kv, ns.q_obs, w, pool, budget, want_scores=True)
+    torch.cuda.synchronize()
+    assert (ns.max_prompt - w) % 2 == 1
+    o_sel, o_cnt = osnap.select_from_scores(host(scores).astype(np.float64), ns.prompt_lens_np, w,
+                                            pool, budget)
+    np.testing.assert_array_equal(host(cnt), o_cnt)
+    np.testing.assert_array_equal(host(sel), o_sel)
