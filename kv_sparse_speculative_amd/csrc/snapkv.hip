@@ -364,11 +364,11 @@ __global__ __launch_bounds__(1024) void snap_topk_kernel(SnapArgs a) {
         // i holds position j0 - 4 + i. Thread t pools positions j0 + 4t .. j0 + 4t + 3 from the
         // 12 words 4t .. 4t + 11 (three 16-byte reads) with three-input maxima.
         // Every load of the loop is unconditional, so the compiler counts them and waits for
-        // each tile's loads only where they are used. A whole tile's pooled values go out as one
-        // 16-byte store per lane (when the row is 16-byte aligned); the tile holding position n - 1 uses buffer stores that the
-        // hardware drops past n. The loads of the next kAhead tiles are in flight while one is
-        // pooled; the last round may pool up to three tiles past the end, whose stores are all
-        // dropped.
+        // each tile's loads only where they are used. A whole tile's pooled values go out as
+        // one 16-byte store per lane (when the row is 16-byte aligned); the tile holding
+        // position n - 1 uses buffer stores that the hardware drops past n. The loads of the
+        // next kAhead tiles are in flight while one is pooled; the last round may pool up to
+        // three tiles past the end, whose stores are all dropped.
         constexpr int kAhead = 4;
         float* tile = reinterpret_cast<float*>(cand_v);
         const int ntiles = (n + kTile - 1) / kTile;
