@@ -35,6 +35,9 @@ namespace {
 
 constexpr int kW = 4;              // waves per workgroup
 constexpr unsigned kBadRow = 0xffffffffu;
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format); with stride 0 and num_records
+// in bytes, an access at or past num_records reads 0.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const uint4& u) {
     bf16x8 r;
@@ -121,8 +124,9 @@ __device__ bool stage_prologue(const SnapArgs& a, int b, int g, int k0, int k1, 
 // lane (m16, q4) of k-step ks holding row m16, dims ks*32 + q4*8 .. +7 (MFMA operand order).
 // c0 is wave-uniform and a multiple of 16, so each 16-key tile's block base is one uniform LDS
 // read. Keys outside [k0, k1) or with a bad block load row 0 and are reported as masked.
-// (Loading whole rows per instruction and reordering through LDS measured slower here: with the
-// score arithmetic in the loop the access pattern is not what limits these passes.)
+// (For the passes over many row tiles, loading whole rows per instruction and reordering
+// through LDS measured slower: with their score arithmetic in the loop the access pattern is
+// not what limits them. The one-tile stored-score pass uses load_k_rows instead.)
 template <int D>
 __device__ __forceinline__ void load_k(const uint16_t* kp, const unsigned* tab, int bs, int sh,
                                        int blk0, int c0, int k1, int m16, int q4,
@@ -139,6 +143,69 @@ __device__ __forceinline__ void load_k(const uint16_t* kp, const unsigned* tab, 
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
             kr[kt][ks] = *reinterpret_cast<const uint4*>(kp + off + ks * 32);   // 64 B per row: plain
+    }
+}
+
+// The same chunk loaded whole rows per instruction with nontemporal loads: instruction ks of
+// tile kt covers the 1 KB of rows ks * RPI .. + RPI - 1 of the tile (RPI = 1024 / (2 D)), lane l
+// holding row ks * RPI + l / (D / 8), dims (l % (D / 8)) * 8 .. +7. rows_to_operands turns it
+// into load_k's layout. okm as in load_k. The valid rows of a tile are a prefix (the tile lies in
+// one block and the range ends at k1), so each tile is read through a buffer resource covering
+// just them: masked rows read as zero without a memory access, and one lane offset serves all
+// loads.
+template <int D>
+__device__ __forceinline__ void load_k_rows(const uint16_t* kp, const unsigned* tab, int bs, int sh,
+                                            int blk0, int c0, int k1, int lane,
+                                            uint4 (&kr)[2][D / 32], unsigned (&okm)[2]) {
+    constexpr int kNontemporal = 2;                      // cache-policy bits of the load
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        // Branch-free, so that the loads of both tiles stay in one block and the compiler can
+        // count them exactly when it waits for a chunk: the table read is clamped into the
+        // table (a tile past k1 discards what it reads).
+        const int t0 = c0 + kt * 16;
+        const int blk = div_bs(t0, bs, sh);
+        const unsigned tv = __builtin_amdgcn_readfirstlane(
+            tab[min(max(blk - blk0, 0), kSnapTableEntries)]);
+        const unsigned base = t0 < k1 ? tv : kBadRow;
+        const int n_ok = base != kBadRow ? min(k1 - t0, 16) : 0;
+        okm[kt] = n_ok >= 16 ? 0xffffu : (1u << n_ok) - 1u;
+        const unsigned row0 = n_ok > 0 ? base + (unsigned)(t0 - blk * bs) : 0u;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(kp + (size_t)row0 * D), (short)0, n_ok * D * 2, kBufferWord3);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + ks * 1024, 0,
+                                                                    kNontemporal);
+            kr[kt][ks] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    }
+}
+
+// Reorder a chunk from load_k_rows' layout into MFMA operand order through a wave-private LDS
+// tile of 16 rows (D / 8 16-byte pieces each), one 16-key tile at a time. Piece p of row j is
+// kept in slot p ^ ((j / RP) % (D / 8)), RP = rows per 256 bytes, so that the row-wise writes
+// and the operand reads (one piece of each of 16 rows) both meet every bank once per 16 lanes.
+// The wave's DS instructions execute in order, so a tile's reads see its writes and the next
+// tile's writes come after them.
+template <int D>
+__device__ __forceinline__ void rows_to_operands(uint4* buf, int lane, uint4 (&kr)[2][D / 32]) {
+    constexpr int LPR = D / 8, RPI = 64 / LPR, RP = 128 / D;
+    const int m16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        wave_lds_order();
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const int j = ks * RPI + lane / LPR, p = lane % LPR;
+            buf[j * LPR + (p ^ ((j / RP) % LPR))] = kr[kt][ks];
+        }
+        wave_lds_order();
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const int p = ks * 4 + q4;
+            kr[kt][ks] = buf[m16 * LPR + (p ^ ((m16 / RP) % LPR))];
+        }
     }
 }
 
@@ -209,7 +276,7 @@ __device__ __forceinline__ void read_q(const uint4* qs, int t, int lane, uint4 (
 // workgroups per CU costs two spilled registers and runs the pass ~10% faster (256 rows at a
 // 100k context: SnapKV select 2.98-3.08 -> 2.71 ms, same selection).
 template <int D, int NT, bool STORE>
-__global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(SnapArgs a) {
+__global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : STORE ? 3 : 1) void snap_rowstats_mfma(SnapArgs a) {
     static_assert(!STORE || NT == 1, "stored scores use one row tile");
     constexpr int KS = D / 32;
 
@@ -238,14 +305,22 @@ __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(
         __syncthreads_or(!fits || stage_prologue<D, NT, kSnapTableEntries + 1>(
                                       a, b, g, k0, kend, tab, qs, nullptr, nullptr)) != 0;
 
-    // The first two chunks are issued after the barrier (they need the block bases).
+    // The first two chunks are issued after the barrier (they need the block bases). With one
+    // row tile the pass has little arithmetic per byte, and there whole-row nontemporal loads
+    // reordered through LDS beat operand-order loads (the per-step Top-K search's K read).
     const uint16_t* kp = static_cast<const uint16_t*>(a.k);
     constexpr int stride = kW * 32;
+    __shared__ uint4 kreorder[STORE ? kW * 16 * (D / 8) : 1];
+    uint4* kbuf = kreorder + (STORE ? wid * 16 * (D / 8) : 0);
+    auto issue = [&](int c0, uint4 (&kr)[2][KS], unsigned (&okm)[2]) {
+        if constexpr (STORE) load_k_rows<D>(kp, tab, bs, sh, blk0, c0, kend, lane, kr, okm);
+        else load_k<D>(kp, tab, bs, sh, blk0, c0, kend, m16, q4, kr, okm);
+    };
     uint4 kA[2][KS], kB[2][KS];
     unsigned okA[2], okB[2];
     int c = k0 + wid * 32;
-    load_k<D>(kp, tab, bs, sh, blk0, c, kend, m16, q4, kA, okA);
-    load_k<D>(kp, tab, bs, sh, blk0, c + stride, kend, m16, q4, kB, okB);
+    issue(c, kA, okA);
+    issue(c + stride, kB, okB);
 
     // Per lane: online (max, sum) of the scores it holds for row t*16 + m16; the maximum is
     // kept negated (nm = -m) so the exponent is one fma.
@@ -345,7 +420,8 @@ __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(
             __builtin_amdgcn_sched_barrier(0);      // keep the per-tile issue order
         }
     };
-    auto step = [&](int c0, const uint4 (&kr)[2][KS], const unsigned (&okm)[2]) {
+    auto step = [&](int c0, uint4 (&kr)[2][KS], const unsigned (&okm)[2]) {
+        if constexpr (STORE) rows_to_operands<D>(kbuf, lane, kr);
         // Uniform: every key of the chunk is valid and visible to every row.
         if ((okm[0] & okm[1]) == 0xffffu && c0 + 31 < causal_from)
             consume(std::true_type{}, c0, kr, okm);
@@ -356,10 +432,10 @@ __global__ __launch_bounds__(kW * 64, NT >= 16 ? 2 : 1) void snap_rowstats_mfma(
     // Two chunks in flight per wave: consume one, then reissue its registers two chunks ahead.
     for (; c < kend; c += 2 * stride) {
         step(c, kA, okA);
-        load_k<D>(kp, tab, bs, sh, blk0, c + 2 * stride, kend, m16, q4, kA, okA);
+        issue(c + 2 * stride, kA, okA);
         if (c + stride >= kend) break;
         step(c + stride, kB, okB);
-        load_k<D>(kp, tab, bs, sh, blk0, c + 3 * stride, kend, m16, q4, kB, okB);
+        issue(c + 3 * stride, kB, okB);
     }
 
     // Merge the 4 lane groups (xor 16, 32) and then the waves, per row.
