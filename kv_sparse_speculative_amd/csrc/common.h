@@ -37,9 +37,6 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Compiler-level memory barrier: keeps LDS stores and the loads that read them (from other
-// lanes of the same wave) in program order; the LDS unit executes one wave's DS instructions
-// in order, so no hardware wait is needed between them.
 // 16-byte load of data the call reads exactly once (K/V rows, logits): a nontemporal load.
 // On gfx950 a stream of these keeps ~7.1 TB/s of HBM read rate, against ~6.2 TB/s for plain
 // loads that allocate in the caches.
@@ -54,6 +51,9 @@ __device__ __forceinline__ float4 load_stream_f4(const void* p) {
                        __uint_as_float(u.w));
 }
 
+// Compiler-level memory barrier: keeps LDS stores and the loads that read them (from other
+// lanes of the same wave) in program order; the LDS unit executes one wave's DS instructions
+// in order, so no hardware wait is needed between them.
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
 // x / bs with a shift when the block size is a power of two (sh >= 0), else a division.

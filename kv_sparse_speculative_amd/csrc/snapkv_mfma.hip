@@ -8,7 +8,8 @@
 // Both passes stream K once each from HBM (K rows as 16-byte lane loads, double-buffered in
 // registers; physical rows from a per-workgroup LDS table of block bases) and keep the
 // observation queries in LDS laid out in MFMA operand order, so every operand read is one
-// conflict-free 1 KB ds_read_b128 per wave.
+// conflict-free 1 KB ds_read_b128 per wave. The one-row-tile pass 1 that also stores its scores
+// (for a pass 2 that reads them instead of K) loads whole K rows and reorders them in LDS.
 //   pass 1: S^T tile (16 keys x 16 rows) = K . Q^T, K as the A operand. Each lane keeps an
 //           online (max, sum) of the scores it holds for its row; the 4 lane groups and the 4
 //           waves are merged once at the end.
