@@ -161,9 +161,8 @@ __device__ __forceinline__ void load_k_rows(const uint16_t* kp, const unsigned* 
     constexpr int kNontemporal = 2;                      // cache-policy bits of the load
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-        // Branch-free, so that the loads of both tiles stay in one block and the compiler can
-        // count them exactly when it waits for a chunk: the table read is clamped into the
-        // table (a tile past k1 discards what it reads).
+        // No branch around the loads: the table read is clamped into the table (a tile past k1
+        // discards what it reads) and the rest are selects on wave-uniform values.
         const int t0 = c0 + kt * 16;
         const int blk = div_bs(t0, bs, sh);
         const unsigned tv = __builtin_amdgcn_readfirstlane(
