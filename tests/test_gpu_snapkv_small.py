@@ -1,5 +1,6 @@
 """GPU parity of SnapKV selection with few observation rows per KV head (R = G * w <= 16),
-where the first pass keeps its scaled scores and the second pass reads them instead of K:
+where the first pass keeps its scaled scores and the second pass reads them instead of K (at
+head_dim 128 and 64):
 scores within float32 rounding of the oracle, the selection bit-exact on the GPU's own scores,
 the same result through the path that re-reads K (unaligned workspace), and the NaN poisoning
 of a sequence whose block table holds an invalid block id."""
@@ -13,22 +14,29 @@ import torch
 import oracle.snapkv as osnap
 from kv_sparse_speculative_amd import kvss
 from kv_sparse_speculative_amd.synth import generate
-from kv_sparse_speculative_amd.workloads import WORKLOADS
+from kv_sparse_speculative_amd.workloads import WORKLOADS, Workload
 
 from _helpers import host
 
 pytestmark = pytest.mark.gpu
 
+# head_dim 64 (two rows per 256 bytes in the stored pass's LDS reorder), G = 4, shuffled pages,
+# prompts with ragged 16-key tails
+D64 = Workload("bf16_d64_g4_small", "bf16", 3, 16, 4, 64, (301, 1111), 3, (4, 60), (96, 4, 5),
+               1000, block_size=16, shuffled_blocks=True, seed=2101)
+WL = dict(WORKLOADS, **{D64.name: D64})
+
 CASES = [("llama8b_ctx8k", 1, {"batch": 2}), ("llama8b_ctx8k", 3, {"batch": 2}),
          ("llama8b_ctx8k", 4, {"batch": 3, "prompt": (37, 900)}),     # R = 16
          ("llama8b_ctx8k", 5, {"batch": 2}),                          # R = 20: re-reads K
          ("qwen32b_ragged", 3, {"batch": 3}),                         # G = 5: R = 15
-         ("llama8b_ctx32k", 2, {"batch": 1})]
+         ("llama8b_ctx32k", 2, {"batch": 1}),
+         (D64.name, 1, {}), (D64.name, 4, {})]                        # head_dim 64: R = 4, 16
 
 
 def _setup(name, w, kw):
     torch.manual_seed(0)
-    ns = generate(WORKLOADS[name], device="cuda", parts=("attn",), **kw)
+    ns = generate(WL[name], device="cuda", parts=("attn",), **kw)
     q_obs = ns.q_obs[:, :, -w:].contiguous()
     P = ns.prompt_lens_np
     kv = kvss.PagedKV(ns.k_cache, ns.v_cache, ns.block_table, ns.prompt_lens, int(P.max()))
